@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the low-M split-K bf16 GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the whole hot path (lowm_gemm_splitk: W stream, MFMA,
+wavefront reduction, split-K publish/fold, bf16 store) on one set of inputs.
+The workload is the headline shape of the TensorRT-LLM PR "Fix two
+synchronization gaps in the MiniMax M3 low-M split-K GEMM" (Hardware
+verification): M 4, N 6144, K 4096, split_k 2, with synthetic N(0,1)
+activations and N(0,0.02) weights.  Inputs are resident in HBM before timing;
+the calls rotate through a pool of input sets larger than twice the 256 MB
+MALL so the weights stream from HBM rather than the Infinity Cache.
+
+Prints one JSON line on stdout; details go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+MALL_BYTES = 256 << 20          # Infinity Cache
+KERNEL_SOURCE = ROOT / "split_bf16_gemm_amd" / "csrc" / "lowm_splitk.hip"
+PMC_FILE = ROOT / "profiles" / "pmc_traffic.json"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(M: int, N: int, K: int, S: int) -> int:
+    """2KN (W once) + 2MK (A once) + 2MN (bf16 C) + 4MN(2S-1) workspace
+    (every rank writes its fp32 partial, the owner reads the other S-1)."""
+    ws = 4 * M * N * (2 * S - 1) if S > 1 else 0
+    return 2 * K * N + 2 * M * K + 2 * M * N + ws
+
+
+def source_hash() -> str:
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()[:16]
+
+
+def parse_tactic(text):
+    from split_bf16_gemm_amd import binding
+    if not text:
+        return None
+    stage, rows, unroll, stages = text.split(":")
+    return binding.tactic(stage, int(rows), int(unroll), int(stages))
+
+
+class Pool:
+    """Input sets (A, W, C, workspace) on the device, rotated call by call."""
+
+    def __init__(self, lib, wl, sets: int, dev):
+        import torch
+        import workloads
+        self.wl = wl
+        M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
+        A0, W0 = workloads.make_inputs(wl)
+        g = torch.Generator(device=dev)
+        g.manual_seed(wl.seed_w + 7919)
+        self.sets = []
+        for i in range(sets):
+            if i == 0:
+                A, W = A0.to(dev), W0.to(dev)
+            else:
+                A = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+                W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = lib.make_workspace(M, N, K, S, dev)
+            self.sets.append((A, W, C, ws))
+        torch.cuda.synchronize()
+        self.ptrs = [(A.data_ptr(), W.data_ptr(), C.data_ptr(), ws.data_ptr() if ws is not None else 0)
+                     for (A, W, C, ws) in self.sets]
+
+
+def make_caller(lib, wl, tactic, stream_handle):
+    raw = lib.call_raw
+    M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
+
+    def call(p):
+        rc = raw(p[0], p[1], p[2], M, N, K, S, p[3], stream_handle, False, tactic)
+        if rc:
+            lib.check(rc)
+    return call
+
+
+def time_loop(call, ptrs, steps):
+    """Elapsed time of `steps` back-to-back calls between two events (us/call)."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        call(ptrs[i % len(ptrs)])
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps
+
+
+def time_each(call, ptrs, steps):
+    """Average duration of one launch, from an event pair around each launch."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record()
+        call(ptrs[i % len(ptrs)])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    return statistics.mean(d), statistics.median(d)
+
+
+def time_graph(make_call, ptrs, steps, dev):
+    """The same loop captured once in a HIP graph and replayed (us/call)."""
+    import torch
+    s = torch.cuda.Stream(device=dev)
+    call = make_call(s.cuda_stream)       # launches must go to the capturing stream
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(steps):
+            call(ptrs[i % len(ptrs)])
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps
+
+
+def hbm_read_ceiling(pool, dev, reps=5):
+    """GB/s of a plain streaming read of each set's W, rotating like the GEMM."""
+    import torch
+    from split_bf16_gemm_amd import BwProbe
+    bw = BwProbe()
+    blocks = 256 * 8
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    Ws = [s[1] for s in pool.sets]
+    for W in Ws:
+        bw.read(W, sink, blocks)
+    res = []
+    for _ in range(reps):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        n = 0
+        for _ in range(4):
+            for W in Ws:
+                bw.read(W, sink, blocks)
+                n += 1
+        end.record()
+        end.synchronize()
+        us = start.elapsed_time(end) * 1e3 / n
+        res.append(Ws[0].numel() * 2 / us / 1e3)
+    return statistics.median(res)
+
+
+def pmc_traffic(wl, tactic_dict, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    if not PMC_FILE.exists():
+        return None
+    try:
+        rec = json.loads(PMC_FILE.read_text())
+    except ValueError:
+        return None
+    if rec.get("source_sha") != source_hash() or rec.get("workload") != wl.name:
+        return None
+    if rec.get("tactic") != tactic_dict:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The fp64 oracle on the host cores: full products of the workload,
+    repeated until about budget_s seconds of CPU work."""
+    import oracle
+    import workloads
+    A, W = workloads.make_inputs(wl)
+    a, w = workloads.bits(A), workloads.bits(W)
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        orc.gemm(a, w)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    b = algorithmic_bytes(wl.M, wl.N, wl.K, wl.split_k)
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full {wl.name} products (fp64, single thread), "
+                      f"{dt * 1e3:.1f} ms each",
+            "ms_per_call": round(dt * 1e3, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="m4_n6144_k4096_s2")
+    ap.add_argument("--tactic", default=None, help="stage:rows:unroll:stages, e.g. reg:16:4:3")
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import split_bf16_gemm_amd as sbg
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    lib = sbg.load()
+    wl = workloads.by_name(args.workload)
+    M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
+    tactic = parse_tactic(args.tactic)
+    tac = tactic if tactic is not None else lib.pick_tactic(M, N, K, S)
+    per_set = 2 * K * N + 2 * M * K + 2 * M * N + lib.workspace_bytes(M, N, K, S)
+    sets = max(2, math.ceil(2 * MALL_BYTES / per_set) + 1)
+    log(f"workload {wl.name}: tactic {tac!r}, pool {sets} sets x {per_set / 1e6:.1f} MB")
+    pool = Pool(lib, wl, sets, dev)
+    stream = torch.cuda.current_stream(dev)
+    call = make_caller(lib, wl, tactic, stream.cuda_stream)
+
+    for i in range(args.warmup):
+        call(pool.ptrs[i % sets])
+    torch.cuda.synchronize()
+
+    us_loop = statistics.median(time_loop(call, pool.ptrs, args.steps) for _ in range(args.reps))
+    each = [time_each(call, pool.ptrs, args.steps) for _ in range(args.reps)]
+    us_kernel = statistics.median(e[0] for e in each)
+    us_kernel_med = statistics.median(e[1] for e in each)
+    us_warm = statistics.median(time_loop(call, pool.ptrs[:1], args.steps) for _ in range(args.reps))
+    us_graph = None
+    if not args.no_graph:
+        try:
+            us_graph = statistics.median(
+                time_graph(lambda h: make_caller(lib, wl, tactic, h), pool.ptrs, args.steps, dev)
+                for _ in range(args.reps))
+        except Exception as e:  # graph capture is an extra figure, not the metric
+            log(f"graph timing skipped: {e}")
+    ceiling = hbm_read_ceiling(pool, dev)
+
+    nbytes = algorithmic_bytes(M, N, K, S)
+    gbps = nbytes / us_loop / 1e3
+    achieved = nbytes / us_kernel / 1e3
+    log(f"us/call {us_loop:.3f} (plain loop), kernel {us_kernel:.3f} avg / {us_kernel_med:.3f} "
+        f"median (event pairs), graph {us_graph}, MALL-warm {us_warm:.3f}; "
+        f"HBM read ceiling {ceiling:.0f} GB/s")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    out = {
+        "metric": "µs/call + achieved HBM GB/s (% of peak), M=4 N=6144 K=4096 split_k=2",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_loop / 1e3, 6),
+        "us_per_call": round(us_loop, 3),
+        "pct_of_peak_hbm": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "M": M, "N": N, "K": K, "split_k": S,
+            "tactic": tac.as_dict(), "bytes_per_call": nbytes, "pool_sets": sets,
+            "seeds": {"a": wl.seed_a, "w": wl.seed_w},
+        },
+        "timings_us": {
+            "plain_loop_per_call": round(us_loop, 3),
+            "kernel_avg_event_pairs": round(us_kernel, 3),
+            "kernel_median_event_pairs": round(us_kernel_med, 3),
+            "graph_replay_per_call": None if us_graph is None else round(us_graph, 3),
+            "mall_warm_single_set_not_hbm": round(us_warm, 3),
+        },
+        "hbm_read_ceiling_gbps": round(ceiling, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": pmc_traffic(wl, tac.as_dict(), nbytes),
+        },
+        "cpu_baseline": cpu,
+        "kernel_source_sha": source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

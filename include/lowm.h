@@ -1,0 +1,146 @@
+/*
+ * lowm.h -- C ABI of the low-M split-K bf16 GEMM for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (TensorRT-LLM PR "Fix two synchronization gaps in the MiniMax
+ * M3 low-M split-K GEMM", Description item 2 and Hardware verification):
+ *
+ *     C[m][n] = sum_{k=0}^{K-1} A[m][k] * W[n][k]        (C = A * W^T)
+ *
+ * with A [M, K] and W [N, K] bf16, fp32 accumulation and a bf16 (or fp32)
+ * result.  The K range is cut into split_k equal contiguous slices; each slice
+ * ("rank") produces an fp32 partial of the output tile and one owner adds the
+ * partials, always in rank order 0, 1, ..., split_k-1, then rounds once to
+ * bf16 (round-to-nearest-even) and is the only writer of C.  The owner is the
+ * last rank of the tile to arrive (a per-tile counter in the workspace), so no
+ * workgroup ever waits for another and any grid size is deadlock-free.
+ *
+ * Layouts: A, W and C are dense row-major with no padding: element (m, k) of A
+ * at A + m*K + k, (n, k) of W at W + n*K + k, (m, n) of C at C + m*N + n.
+ *
+ * Ownership: the caller owns every buffer.  The library allocates nothing,
+ * frees nothing and keeps no mutable global state (a per-device table of
+ * compute-unit counts is read once).  All entry points that launch work are
+ * asynchronous on `stream` (a hipStream_t; NULL is the null stream): they
+ * validate their arguments on the host before any HIP call, enqueue one
+ * kernel and return.  Execution errors surface at the caller's next
+ * synchronisation.
+ *
+ * Workspace (split_k > 1 only): an opaque device buffer of
+ * lowm_gemm_splitk_workspace_bytes(M, N, K, split_k) bytes, 256-byte aligned,
+ * holding one arrival counter per output tile followed by the fp32 partials.
+ * Zero it once before first use (hipMemset).  Every launch that completes
+ * leaves all counters at zero again (the owner resets its tile's counter), so
+ * the workspace can be reused by the next launch without clearing; the
+ * partial region is scratch and may hold anything between launches.  One
+ * workspace per in-flight launch: launches that overlap in time (two streams)
+ * must not share one.  After a launch that did not complete, zero it again.
+ *
+ * Errors: every int-returning function returns LOWM_OK (0) or a negative
+ * LOWM_ERR_* code; lowm_strerror() names it and lowm_last_hip_error() gives
+ * the hipError_t behind LOWM_ERR_LAUNCH on the calling thread.
+ */
+#ifndef LOWM_H
+#define LOWM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWM_OK 0
+/* A NULL operand pointer, M, N or K <= 0, or split_k < 1. */
+#define LOWM_ERR_INVALID_ARG (-1)
+/* Outside what the kernels support: M > 64 (the low-M regime); K not a
+ * multiple of 8 * split_k (every rank's slice must be a non-empty whole number
+ * of 16-byte vectors); split_k > 256; A, W or the workspace not 16-byte
+ * aligned; C not aligned to its element size; a tactic the build lacks. */
+#define LOWM_ERR_UNSUPPORTED (-2)
+/* split_k > 1 with a NULL workspace. */
+#define LOWM_ERR_WORKSPACE (-3)
+/* The kernel launch itself failed; see lowm_last_hip_error(). */
+#define LOWM_ERR_LAUNCH (-4)
+
+/* Largest M the kernels accept. */
+#define LOWM_MAX_M 64
+/* Largest split_k the kernels accept. */
+#define LOWM_MAX_SPLIT_K 256
+
+/*
+ * C (bf16 [M, N]) = A (bf16 [M, K]) * W (bf16 [N, K])^T, fp32 accumulation,
+ * split_k equal K slices folded in rank order by the last-arriving rank.
+ * `workspace` may be NULL when split_k == 1.  `stream` is a hipStream_t.
+ */
+int lowm_gemm_splitk(const void* A, const void* W, void* C,
+                     int M, int N, int K, int split_k,
+                     void* workspace, void* stream);
+
+/*
+ * The same product with an fp32 result: C is float [M, N].  Same kernel and
+ * summation order; only the final store differs, so the bf16 entry point's
+ * output is exactly this result rounded to nearest-even.
+ */
+int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C,
+                            int M, int N, int K, int split_k,
+                            void* workspace, void* stream);
+
+/*
+ * Bytes of workspace a launch with these sizes needs: 0 when split_k == 1,
+ * else the counters (rounded up to 256 bytes) plus the fp32 partials.  Returns
+ * 0 as well for arguments the launch would reject.
+ */
+size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k);
+
+/* Static text naming an error code. */
+const char* lowm_strerror(int code);
+
+/* hipError_t of the most recent failed launch on the calling thread (0 if
+ * none). */
+int lowm_last_hip_error(void);
+
+/*
+ * Tactic: how a launch tiles the problem.  lowm_gemm_splitk picks one from
+ * (M, N, K, split_k); the _ex entry points take it explicitly, for tuning
+ * sweeps and for tests that cover every variant.  Any tactic gives a correct
+ * result; the summation order (and so the low bits of random-input results)
+ * depends on it.
+ *   stage      LOWM_STAGE_LDS: W goes global -> LDS ring of `stages` stages
+ *              shared by the workgroup (direct-to-LDS loads), barrier before a
+ *              stage is refilled; LOWM_STAGE_REG: W goes global -> registers,
+ *              double-buffered per wavefront.
+ *   rows       W rows (output columns) per workgroup tile: 16, 32 or 64.
+ *   waves      wavefronts per workgroup: 4 (the K slice of a rank is split
+ *              between them and their sums are added in wave order).
+ *   unroll     32-wide K chunks each wavefront takes per step: 1, 2 or 4.
+ *   stages     LDS ring depth for LOWM_STAGE_LDS: 2, 3 or 4.
+ */
+#define LOWM_STAGE_LDS 0
+#define LOWM_STAGE_REG 1
+typedef struct lowm_tactic {
+    int stage;
+    int rows;
+    int waves;
+    int unroll;
+    int stages;
+} lowm_tactic;
+
+/* The tactic lowm_gemm_splitk would use for these sizes (written to *out).
+ * Returns LOWM_OK or an error code for sizes it would reject. */
+int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out);
+
+/* lowm_gemm_splitk / _f32out with an explicit tactic (NULL: the default).
+ * LOWM_ERR_UNSUPPORTED for a tactic this build does not provide. */
+int lowm_gemm_splitk_ex(const void* A, const void* W, void* C,
+                        int M, int N, int K, int split_k,
+                        void* workspace, void* stream, const lowm_tactic* tactic);
+int lowm_gemm_splitk_f32out_ex(const void* A, const void* W, float* C,
+                               int M, int N, int K, int split_k,
+                               void* workspace, void* stream,
+                               const lowm_tactic* tactic);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOWM_H */

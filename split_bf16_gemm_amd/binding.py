@@ -1,0 +1,236 @@
+"""ctypes binding of the C ABI in include/lowm.h.
+
+Argument marshalling only: every step of the product runs in the HIP kernels
+of liblowm.so.  PyTorch supplies device memory and the current stream.  There
+is no fallback: when the library is not built, or a call fails, this raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+LIBDIR = Path(__file__).resolve().parent / "_lib"
+
+LOWM_OK = 0
+LOWM_ERR_INVALID_ARG = -1
+LOWM_ERR_UNSUPPORTED = -2
+LOWM_ERR_WORKSPACE = -3
+LOWM_ERR_LAUNCH = -4
+LOWM_STAGE_LDS = 0
+LOWM_STAGE_REG = 1
+MAX_M = 64
+MAX_SPLIT_K = 256
+
+# stall sites of the stress build
+SITE_ENTRY = 1
+SITE_STAGE_READ = 2
+SITE_REDUCE = 4
+SITE_PUBLISH = 8
+SITE_FOLD = 16
+
+
+class Tactic(ctypes.Structure):
+    _fields_ = [("stage", ctypes.c_int), ("rows", ctypes.c_int), ("waves", ctypes.c_int),
+                ("unroll", ctypes.c_int), ("stages", ctypes.c_int)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+    def __repr__(self) -> str:
+        st = "lds" if self.stage == LOWM_STAGE_LDS else "reg"
+        return (f"Tactic({st}, rows={self.rows}, waves={self.waves}, "
+                f"unroll={self.unroll}, stages={self.stages})")
+
+
+def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 4) -> Tactic:
+    return Tactic(LOWM_STAGE_LDS if stage == "lds" else LOWM_STAGE_REG, rows, waves,
+                  unroll, stages)
+
+
+class LowmError(RuntimeError):
+    def __init__(self, code: int, message: str, hip_error: int = 0):
+        super().__init__(f"lowm error {code}: {message}"
+                         + (f" (hipError {hip_error})" if hip_error else ""))
+        self.code = code
+        self.hip_error = hip_error
+
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_TP = ctypes.POINTER(Tactic)
+
+
+class Library:
+    """One loaded build of the GEMM library (default or stress)."""
+
+    EXPORTS = ("lowm_gemm_splitk", "lowm_gemm_splitk_f32out", "lowm_gemm_splitk_workspace_bytes",
+               "lowm_strerror", "lowm_last_hip_error", "lowm_pick_tactic",
+               "lowm_gemm_splitk_ex", "lowm_gemm_splitk_f32out_ex")
+
+    def __init__(self, path: Path):
+        if not path.exists():
+            raise RuntimeError(
+                f"{path.name} is not built; run `python -m split_bf16_gemm_amd.build` "
+                "(there is no CPU fallback)")
+        self.path = path
+        lib = ctypes.CDLL(str(path))
+        for name in ("lowm_gemm_splitk", "lowm_gemm_splitk_f32out"):
+            fn = getattr(lib, name)
+            fn.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]
+            fn.restype = _i
+        for name in ("lowm_gemm_splitk_ex", "lowm_gemm_splitk_f32out_ex"):
+            fn = getattr(lib, name)
+            fn.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _TP]
+            fn.restype = _i
+        lib.lowm_gemm_splitk_workspace_bytes.argtypes = [_i, _i, _i, _i]
+        lib.lowm_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
+        lib.lowm_strerror.argtypes = [_i]
+        lib.lowm_strerror.restype = ctypes.c_char_p
+        lib.lowm_last_hip_error.argtypes = []
+        lib.lowm_last_hip_error.restype = _i
+        lib.lowm_pick_tactic.argtypes = [_i, _i, _i, _i, _TP]
+        lib.lowm_pick_tactic.restype = _i
+        self.has_stress = hasattr(lib, "lowm_stress_configure")
+        if self.has_stress:
+            lib.lowm_stress_configure.argtypes = [ctypes.c_uint, _i, _i, _i, _i, _i, ctypes.c_uint]
+            lib.lowm_stress_configure.restype = _i
+        self.lib = lib
+
+    # -- host-only queries ------------------------------------------------
+    def strerror(self, code: int) -> str:
+        return self.lib.lowm_strerror(code).decode()
+
+    def workspace_bytes(self, M: int, N: int, K: int, split_k: int) -> int:
+        return int(self.lib.lowm_gemm_splitk_workspace_bytes(M, N, K, split_k))
+
+    def pick_tactic(self, M: int, N: int, K: int, split_k: int) -> Tactic:
+        t = Tactic()
+        self.check(self.lib.lowm_pick_tactic(M, N, K, split_k, ctypes.byref(t)))
+        return t
+
+    def check(self, rc: int):
+        if rc != LOWM_OK:
+            hip = self.lib.lowm_last_hip_error() if rc == LOWM_ERR_LAUNCH else 0
+            raise LowmError(rc, self.strerror(rc), hip)
+
+    # -- raw calls (pointers as ints) ------------------------------------
+    def call_raw(self, A: int, W: int, C: int, M: int, N: int, K: int, split_k: int,
+                 workspace: int, stream: int, f32out: bool = False,
+                 tactic: Optional[Tactic] = None) -> int:
+        if tactic is None:
+            fn = self.lib.lowm_gemm_splitk_f32out if f32out else self.lib.lowm_gemm_splitk
+            return fn(A, W, C, M, N, K, split_k, workspace, stream)
+        fn = self.lib.lowm_gemm_splitk_f32out_ex if f32out else self.lib.lowm_gemm_splitk_ex
+        return fn(A, W, C, M, N, K, split_k, workspace, stream, ctypes.byref(tactic))
+
+    # -- torch-facing call -------------------------------------------------
+    def gemm(self, A: torch.Tensor, W: torch.Tensor, split_k: int = 1,
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             out_dtype: torch.dtype = torch.bfloat16, tactic: Optional[Tactic] = None,
+             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """C = A @ W.T on the GPU (A [M,K], W [N,K] bf16) through the C ABI."""
+        if A.dim() != 2 or W.dim() != 2 or A.shape[1] != W.shape[1]:
+            raise ValueError(f"shapes {tuple(A.shape)} and {tuple(W.shape)} do not chain")
+        if A.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+            raise TypeError("A and W must be bfloat16")
+        if not (A.is_cuda and W.is_cuda):
+            raise ValueError("A and W must be on the GPU")
+        if not (A.is_contiguous() and W.is_contiguous()):
+            raise ValueError("A and W must be contiguous row-major")
+        M, K = A.shape
+        N = W.shape[0]
+        f32out = out_dtype == torch.float32
+        if out is None:
+            out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+        if out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [M, N] tensor of out_dtype")
+        ws_ptr = 0
+        if split_k > 1:
+            need = self.workspace_bytes(M, N, K, split_k)
+            if workspace is None:
+                raise ValueError(f"split_k={split_k} needs a zeroed workspace of {need} bytes "
+                                 "(make_workspace)")
+            if workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+                raise ValueError(f"workspace smaller than {need} bytes")
+            ws_ptr = workspace.data_ptr()
+        s = stream if stream is not None else torch.cuda.current_stream(A.device)
+        rc = self.call_raw(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, split_k,
+                           ws_ptr, s.cuda_stream, f32out, tactic)
+        self.check(rc)
+        return out
+
+    def make_workspace(self, M: int, N: int, K: int, split_k: int,
+                       device="cuda") -> Optional[torch.Tensor]:
+        """A zeroed workspace for these sizes (None when split_k == 1)."""
+        n = self.workspace_bytes(M, N, K, split_k)
+        if n == 0:
+            return None
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+
+    def configure_stress(self, sites: int = 0, rank: int = -1, wave: int = -1,
+                         tile_mod: int = 0, tile_sel: int = 0, step: int = -1,
+                         delay_ns: int = 0):
+        if not self.has_stress:
+            raise RuntimeError(f"{self.path.name} is not a stress build")
+        self.check(self.lib.lowm_stress_configure(sites, rank, wave, tile_mod, tile_sel, step,
+                                                  delay_ns))
+
+
+_libs: dict = {}
+
+
+def load(kind: str = "default") -> Library:
+    """The built library: kind 'default' (liblowm.so) or 'stress'."""
+    if kind not in _libs:
+        name = {"default": "liblowm.so", "stress": "liblowm_stress.so"}[kind]
+        _libs[kind] = Library(LIBDIR / name)
+    return _libs[kind]
+
+
+def gemm(A, W, split_k=1, **kw):
+    return load().gemm(A, W, split_k, **kw)
+
+
+def workspace_bytes(M, N, K, split_k):
+    return load().workspace_bytes(M, N, K, split_k)
+
+
+def make_workspace(M, N, K, split_k, device="cuda"):
+    return load().make_workspace(M, N, K, split_k, device)
+
+
+def counter_bytes(N: int) -> int:
+    """Bytes of the counter region at the start of a workspace (see lowm.h)."""
+    return ((4 * ((N + 15) // 16)) + 255) // 256 * 256
+
+
+class BwProbe:
+    """Streaming read / copy kernels (libbwprobe.so) for the HBM ceiling."""
+
+    def __init__(self):
+        path = LIBDIR / "libbwprobe.so"
+        if not path.exists():
+            raise RuntimeError("libbwprobe.so is not built")
+        lib = ctypes.CDLL(str(path))
+        lib.bwprobe_read.argtypes = [_vp, ctypes.c_size_t, _vp, _i, _vp]
+        lib.bwprobe_read.restype = _i
+        lib.bwprobe_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _i, _vp]
+        lib.bwprobe_copy.restype = _i
+        self.lib = lib
+
+    def read(self, src: torch.Tensor, sink: torch.Tensor, blocks: int):
+        n = src.numel() * src.element_size()
+        rc = self.lib.bwprobe_read(src.data_ptr(), n, sink.data_ptr(), blocks,
+                                   torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"bwprobe_read failed: hipError {rc}")
+
+    def copy(self, src: torch.Tensor, dst: torch.Tensor, blocks: int):
+        n = src.numel() * src.element_size()
+        rc = self.lib.bwprobe_copy(src.data_ptr(), dst.data_ptr(), n, blocks,
+                                   torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"bwprobe_copy failed: hipError {rc}")

@@ -1,0 +1,59 @@
+// bwprobe.hip -- plain streaming kernels that measure the HBM ceiling of the
+// device they run on, and a copy of known size whose profiler byte counters
+// calibrate the counters of the GEMM kernel.  Not part of the GEMM path.
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Every thread reads 16-byte vectors in a grid-stride loop and folds them with
+// xor; one word per thread is written so the loads cannot be dropped.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, size_t n,
+                                                   uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = x0, x2 = x0, x3 = x0;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    x0 ^= src[i];
+    x1 ^= src[i + stride];
+    x2 ^= src[i + 2 * stride];
+    x3 ^= src[i + 3 * stride];
+  }
+  for (; i < n; i += stride) x0 ^= src[i];
+  const u32x4 x = x0 ^ x1 ^ x2 ^ x3;
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = x.x ^ x.y ^ x.z ^ x.w;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src,
+                                                   u32x4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) from `src` with `blocks` workgroups of 256
+// threads; `sink` must hold blocks*256 uint32.  Returns a hipError_t.
+int bwprobe_read(const void* src, size_t bytes, void* sink, int blocks, void* stream) {
+  if (!src || !sink || bytes % 16 || blocks <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
+  return (int)hipGetLastError();
+}
+
+// Copies `bytes` (a multiple of 16) from `src` to `dst`.  Returns a hipError_t.
+int bwprobe_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
+  if (!src || !dst || bytes % 16 || blocks <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

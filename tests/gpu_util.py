@@ -1,0 +1,72 @@
+"""Shared helpers of the GPU tests: run the HIP path, cache oracle results."""
+from __future__ import annotations
+
+import functools
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import split_bf16_gemm_amd as sbg
+import workloads
+from split_bf16_gemm_amd import binding
+
+
+def say(*parts):
+    """Name the case before a GPU step, flushed, so a fault can be placed."""
+    print("[gpu]", *parts, file=sys.stderr, flush=True)
+
+
+def device() -> torch.device:
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm device")
+    return torch.device("cuda:0")
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@functools.lru_cache(maxsize=64)
+def inputs(wl: workloads.Workload):
+    A, W = workloads.make_inputs(wl)
+    return A, W
+
+
+@functools.lru_cache(maxsize=64)
+def oracle_result(wl: workloads.Workload):
+    A, W = inputs(wl)
+    return oracle.gemm(workloads.bits(A), workloads.bits(W))
+
+
+def all_tactics(M: int):
+    """Every tactic this build provides for M activation rows."""
+    out = []
+    for rows in (16, 32, 64):
+        for stage, unroll, stages in [("lds", 2, 4), ("lds", 2, 3), ("lds", 4, 3), ("lds", 1, 4),
+                                      ("reg", 2, 4), ("reg", 4, 3), ("reg", 4, 4), ("reg", 2, 3)]:
+            out.append(binding.tactic(stage, rows, unroll, stages))
+    return out
+
+
+def run(lib, A_cpu, W_cpu, split_k, f32out=False, tactic=None, workspace=None, dev=None):
+    """One launch through the C ABI; returns the output as a CPU tensor.
+
+    Returns None when the build does not provide ``tactic`` for this M."""
+    dev = dev or device()
+    A = A_cpu.to(dev)
+    W = W_cpu.to(dev)
+    M, K = A.shape
+    N = W.shape[0]
+    if workspace is None:
+        workspace = lib.make_workspace(M, N, K, split_k, dev)
+    try:
+        out = lib.gemm(A, W, split_k, workspace=workspace, tactic=tactic,
+                       out_dtype=torch.float32 if f32out else torch.bfloat16)
+    except sbg.LowmError as e:
+        if tactic is not None and e.code == binding.LOWM_ERR_UNSUPPORTED:
+            return None
+        raise
+    torch.cuda.synchronize()
+    return out.cpu()

@@ -1,0 +1,142 @@
+"""The C ABI of include/lowm.h, host side only (no kernel is launched).
+
+Every function the header declares is exported by the built libraries, and
+argument validation returns its documented error before any HIP call: these
+tests hand in fake non-NULL pointers that must never reach a launch.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import split_bf16_gemm_amd as sbg
+from split_bf16_gemm_amd import binding
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "lowm.h"
+
+FAKE = 0x10000      # 16-byte aligned, never dereferenced
+FAKE_ODD = 0x10002  # 2-byte aligned only
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(lowm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sbg.load()
+
+
+@pytest.fixture(scope="module")
+def stress_lib():
+    return sbg.load("stress")
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("lowm_gemm_splitk", "lowm_gemm_splitk_f32out",
+              "lowm_gemm_splitk_workspace_bytes", "lowm_strerror", "lowm_last_hip_error"):
+        assert n in names
+
+
+@pytest.mark.parametrize("kind", ["default", "stress"])
+def test_every_declared_symbol_is_exported(kind):
+    lib = sbg.load(kind)
+    for name in declared_functions():
+        assert hasattr(lib.lib, name), f"{lib.path.name} does not export {name}"
+
+
+def test_stress_build_has_its_hook(lib, stress_lib):
+    assert stress_lib.has_stress
+    assert not lib.has_stress
+
+
+def test_strerror_names_every_code(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.strerror(code) and "unknown" not in lib.strerror(code)
+    assert "unknown" in lib.strerror(-99)
+
+
+def test_workspace_bytes(lib):
+    assert lib.workspace_bytes(4, 6144, 4096, 1) == 0
+    # counters for ceil(N/16) tiles rounded to 256 B, then S*M*round_up(N, 64) fp32
+    assert lib.workspace_bytes(4, 6144, 4096, 2) == 1536 + 2 * 4 * 6144 * 4
+    assert lib.workspace_bytes(4, 2304, 12288, 4) == 768 + 4 * 4 * 2304 * 4
+    assert lib.workspace_bytes(3, 17, 64, 2) == 256 + 2 * 3 * 64 * 4
+    assert lib.workspace_bytes(4, 512, 1024, 3) == 0          # K % (8*3) != 0
+    assert lib.workspace_bytes(65, 512, 1024, 2) == 0         # M > 64
+    assert lib.workspace_bytes(0, 512, 1024, 2) == 0
+    assert sbg.counter_bytes(6144) == 1536
+
+
+def test_pick_tactic_is_valid_for_every_workload(lib):
+    import workloads
+    for wl in workloads.ALL:
+        t = lib.pick_tactic(wl.M, wl.N, wl.K, wl.split_k)
+        assert t.rows in (16, 32, 64) and t.waves == 4
+        assert t.rows >= min(64, 16 * ((wl.M + 15) // 16))
+
+
+def call(lib, A=FAKE, W=FAKE, C=FAKE, M=4, N=64, K=256, S=2, ws=FAKE, f32=False, tac=None):
+    return lib.call_raw(A, W, C, M, N, K, S, ws, 0, f32out=f32, tactic=tac)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_invalid_arguments(lib, f32):
+    assert call(lib, A=0, f32=f32) == binding.LOWM_ERR_INVALID_ARG
+    assert call(lib, W=0, f32=f32) == binding.LOWM_ERR_INVALID_ARG
+    assert call(lib, C=0, f32=f32) == binding.LOWM_ERR_INVALID_ARG
+    assert call(lib, M=0, f32=f32) == binding.LOWM_ERR_INVALID_ARG
+    assert call(lib, N=-1, f32=f32) == binding.LOWM_ERR_INVALID_ARG
+    assert call(lib, K=0, f32=f32) == binding.LOWM_ERR_INVALID_ARG
+    assert call(lib, S=0, f32=f32) == binding.LOWM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_unsupported(lib, f32):
+    assert call(lib, M=65, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, K=260, f32=f32) == binding.LOWM_ERR_UNSUPPORTED       # K % 16 != 0
+    assert call(lib, S=257, K=8 * 257, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, A=FAKE + 8, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, W=FAKE + 4, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, ws=FAKE + 8, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, C=FAKE_ODD + 1, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+
+
+def test_fp32_output_needs_4_byte_alignment(lib):
+    assert call(lib, C=FAKE_ODD, f32=True) == binding.LOWM_ERR_UNSUPPORTED
+
+
+def test_workspace_required_for_split(lib):
+    assert call(lib, ws=0) == binding.LOWM_ERR_WORKSPACE
+    assert call(lib, ws=0, f32=True) == binding.LOWM_ERR_WORKSPACE
+
+
+def test_unknown_tactic_is_unsupported(lib):
+    bad = [binding.tactic("reg", 48, 4, 3), binding.tactic("reg", 16, 3, 3),
+           binding.tactic("lds", 16, 2, 5), binding.tactic("reg", 16, 4, 3, waves=8)]
+    for t in bad:
+        assert call(lib, tac=t) == binding.LOWM_ERR_UNSUPPORTED, t
+
+
+def test_errors_precede_any_hip_call(lib):
+    # validation failures leave no HIP error behind
+    call(lib, M=0)
+    assert lib.lib.lowm_last_hip_error() == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.Library(tmp_path / "liblowm.so")
+
+
+def test_pick_tactic_rejects_bad_sizes(lib):
+    t = binding.Tactic()
+    assert lib.lib.lowm_pick_tactic(65, 64, 256, 1, ctypes.byref(t)) == binding.LOWM_ERR_UNSUPPORTED
+    assert lib.lib.lowm_pick_tactic(4, 64, 256, 0, ctypes.byref(t)) == binding.LOWM_ERR_INVALID_ARG
+    assert lib.lib.lowm_pick_tactic(4, 64, 256, 1, None) == binding.LOWM_ERR_INVALID_ARG

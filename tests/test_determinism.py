@@ -1,0 +1,79 @@
+"""Launch determinism of the split-K fold (headline shape, 20 launches).
+
+The owner of a tile is whichever rank arrives last, which varies from launch
+to launch, but it always adds the partials in rank order, so the output must
+not change in a single bit.  Following the PR "Fix two synchronization gaps
+in the MiniMax M3 low-M split-K GEMM" (Hardware verification: 20 launches per
+configuration, each compared bitwise with the unperturbed output), and so that
+a race which reads a stale partial cannot hide behind identical inputs, the
+launches alternate two input sets and, in the second run, the partial region
+of the workspace is filled with NaN (0xFF bytes) before every launch.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_bf16_gemm_amd as sbg
+import workloads
+from checks import assert_bf16, assert_fp32
+from gpu_util import device, inputs, oracle_result, say, to_bits
+
+pytestmark = pytest.mark.gpu
+
+LAUNCHES = 20
+
+
+def two_sets(wl):
+    other = workloads.Workload(wl.name + "_b", wl.M, wl.N, wl.K, wl.split_k,
+                               seed_a=wl.seed_a + 500, seed_w=wl.seed_w + 500)
+    return [wl, other]
+
+
+@pytest.mark.parametrize("wl", [workloads.HEADLINE, workloads.SPLITK4,
+                                workloads.by_name("sweep_m16_n6144_k4096_s8")],
+                         ids=lambda w: w.name)
+@pytest.mark.parametrize("poison", [False, True], ids=["back_to_back", "nan_poisoned"])
+def test_twenty_launches_bitwise(wl, poison):
+    lib = sbg.load()
+    dev = device()
+    sets = two_sets(wl)
+    ops = [tuple(t.to(dev) for t in inputs(s)) for s in sets]
+    ws = lib.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    part = ws[sbg.counter_bytes(wl.N):]
+    outs = [torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device=dev) for _ in range(LAUNCHES)]
+    say("determinism", wl.name, "poison" if poison else "back-to-back")
+    for i in range(LAUNCHES):
+        if poison:
+            part.fill_(0xFF)
+        A, W = ops[i % 2]
+        lib.gemm(A, W, wl.split_k, out=outs[i], workspace=ws)
+    torch.cuda.synchronize()
+    bits = [to_bits(o) for o in outs]
+    for i in range(2, LAUNCHES):
+        assert np.array_equal(bits[i], bits[i % 2]), f"launch {i} differs from launch {i % 2}"
+    assert not np.array_equal(bits[0], bits[1])
+    for j, s in enumerate(sets):
+        C, S = oracle_result(s)
+        assert_bf16(bits[j], C, S, s.K, oracle.default(), what=f"{s.name} launch {j}")
+    ctr = ws[:sbg.counter_bytes(wl.N)].cpu().numpy()
+    assert not ctr.any()
+
+
+def test_fp32_output_is_deterministic_too():
+    lib = sbg.load()
+    dev = device()
+    wl = workloads.HEADLINE
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = lib.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    say("fp32 determinism")
+    outs = [lib.gemm(A, W, wl.split_k, workspace=ws, out_dtype=torch.float32)
+            for _ in range(LAUNCHES)]
+    torch.cuda.synchronize()
+    ref = outs[0].cpu().numpy()
+    C, S = oracle_result(wl)
+    assert_fp32(ref, C, S)
+    for o in outs[1:]:
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), ref.view(np.uint32))

@@ -1,0 +1,171 @@
+"""Parity of the HIP path with the fp64 oracle, element by element.
+
+Bars (tests/checks.py): integer-valued inputs bit-exact in fp32 and bf16;
+random inputs fp32 within 1e-3 * sum|a||w| and bf16 within one ulp of the
+oracle's round-to-nearest-even value.  Shapes: the integer closed form of the
+Triton issue "warpgroup_mma_wait does not properly synchronize across
+warpgroups" (Describe the bug), the three shapes of the TensorRT-LLM PR "Fix
+two synchronization gaps in the MiniMax M3 low-M split-K GEMM" (Hardware
+verification) at full size in the launch configuration the benchmark times,
+the M x split_k sweep, ragged tails and every tactic the build provides.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_bf16_gemm_amd as sbg
+import workloads
+from checks import assert_bf16, assert_exact_integer, assert_fp32
+from gpu_util import all_tactics, device, inputs, oracle_result, run, say, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    device()
+    return sbg.load()
+
+
+def check_random(lib, wl, tactic=None, what=""):
+    A, W = inputs(wl)
+    C, S = oracle_result(wl)
+    say(what or wl.name, wl.M, wl.N, wl.K, wl.split_k, tactic)
+    c32 = run(lib, A, W, wl.split_k, f32out=True, tactic=tactic)
+    if c32 is None:
+        return None
+    c16 = run(lib, A, W, wl.split_k, f32out=False, tactic=tactic)
+    c32 = c32.numpy()
+    b16 = to_bits(c16)
+    assert_fp32(c32, C, S, what=what or wl.name)
+    v = assert_bf16(b16, C, S, wl.K, oracle.default(), c32, what=what or wl.name)
+    # the two entry points share the kernel and its order: bf16 = RNE(fp32)
+    assert np.array_equal(b16, oracle.round_bf16(c32.astype(np.float64))), what
+    return v
+
+
+def test_closed_form_bit_exact_every_tactic(lib):
+    wl = workloads.INT_EXACT
+    A, W = inputs(wl)
+    C, _ = oracle_result(wl)
+    ran = 0
+    for t in all_tactics(wl.M):
+        say("closed form", t)
+        c32 = run(lib, A, W, wl.split_k, f32out=True, tactic=t)
+        if c32 is None:
+            continue
+        c16 = run(lib, A, W, wl.split_k, f32out=False, tactic=t)
+        assert_exact_integer(c32.numpy(), to_bits(c16), C, oracle.default(), what=repr(t))
+        ran += 1
+    assert ran >= 8
+
+
+def test_closed_form_default_tactic(lib):
+    wl = workloads.INT_EXACT
+    A, W = inputs(wl)
+    C, _ = oracle_result(wl)
+    say("closed form default")
+    c32 = run(lib, A, W, wl.split_k, f32out=True)
+    c16 = run(lib, A, W, wl.split_k)
+    assert_exact_integer(c32.numpy(), to_bits(c16), C, oracle.default(), what="default")
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 100, 384), (16, 64, 1024), (33, 48, 512), (64, 40, 256)])
+def test_integer_inputs_identical_for_every_split(lib, M, N, K):
+    wl = workloads.Workload("int_both", M, N, K, 1, kind="int_both", seed_a=M, seed_w=N)
+    A, W = inputs(wl)
+    C, _ = oracle_result(wl)
+    first = None
+    for s in (1, 2, 4, 8):
+        say("integer split", M, N, K, s)
+        c32 = run(lib, A, W, s, f32out=True)
+        c16 = run(lib, A, W, s)
+        assert_exact_integer(c32.numpy(), to_bits(c16), C, oracle.default(), what=f"S={s}")
+        if first is None:
+            first = to_bits(c16)
+        assert np.array_equal(first, to_bits(c16))
+
+
+@pytest.mark.parametrize("wl", [workloads.HEADLINE, workloads.SPLITK4, workloads.WIDE_N],
+                         ids=lambda w: w.name)
+def test_full_size_pages_shapes(lib, wl):
+    check_random(lib, wl)
+
+
+@pytest.mark.parametrize("wl", workloads.sweep(), ids=lambda w: w.name)
+def test_sweep(lib, wl):
+    check_random(lib, wl)
+
+
+RAGGED = [
+    (1, 1, 8, 1), (1, 1, 16, 2), (3, 17, 64, 2), (4, 15, 32, 4), (5, 1000, 1032, 1),
+    (7, 257, 1032, 3), (17, 33, 520, 5), (31, 16, 64, 8), (48, 127, 4104, 3),
+    (63, 77, 2048, 8), (64, 65, 96, 4), (2, 4097, 40, 5), (9, 300, 8, 1),
+]
+
+
+@pytest.mark.parametrize("M,N,K,S", RAGGED)
+def test_ragged(lib, M, N, K, S):
+    wl = workloads.Workload(f"ragged_{M}_{N}_{K}_{S}", M, N, K, S,
+                            seed_a=M * 7 + S, seed_w=N * 3 + K)
+    check_random(lib, wl)
+
+
+def test_every_tactic_random(lib):
+    wl = workloads.Workload("tactics", 20, 300, 2048, 2, seed_a=77, seed_w=78)
+    ran = 0
+    for t in all_tactics(wl.M):
+        if check_random(lib, wl, tactic=t, what=repr(t)) is not None:
+            ran += 1
+    assert ran >= 8
+
+
+def test_every_tactic_small_m_ragged_k(lib):
+    wl = workloads.Workload("tactics_k", 4, 97, 1032, 3, seed_a=5, seed_w=6)
+    for t in all_tactics(wl.M):
+        check_random(lib, wl, tactic=t, what=repr(t))
+
+
+def test_counters_return_to_zero_and_guard_intact(lib):
+    dev = device()
+    wl = workloads.HEADLINE
+    A, W = inputs(wl)
+    need = lib.workspace_bytes(wl.M, wl.N, wl.K, wl.split_k)
+    guard = 4096
+    ws = torch.zeros(need + guard, dtype=torch.uint8, device=dev)
+    ws[need:] = 0xA5
+    say("counters/guard")
+    for _ in range(3):
+        run(lib, A, W, wl.split_k, workspace=ws)
+    host = ws.cpu().numpy()
+    ctr = host[:sbg.counter_bytes(wl.N)]
+    assert not ctr.any(), "an arrival counter was left non-zero"
+    assert (host[need:] == 0xA5).all(), "the kernel wrote past the workspace"
+
+
+def test_split_one_needs_no_workspace(lib):
+    wl = workloads.Workload("s1", 4, 640, 1024, 1, seed_a=1, seed_w=2)
+    A, W = inputs(wl)
+    C, S = oracle_result(wl)
+    say("split 1, no workspace")
+    out = lib.gemm(A.to(device()), W.to(device()), 1, workspace=None,
+                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_fp32(out.cpu().numpy(), C, S)
+
+
+def test_launch_is_asynchronous_on_the_given_stream(lib):
+    dev = device()
+    wl = workloads.HEADLINE
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = lib.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    s = torch.cuda.Stream(device=dev)
+    say("side stream")
+    with torch.cuda.stream(s):
+        out = lib.gemm(A, W, wl.split_k, workspace=ws, out_dtype=torch.float32)
+    s.synchronize()
+    C, S = oracle_result(wl)
+    assert_fp32(out.cpu().numpy(), C, S)

@@ -1,0 +1,121 @@
+"""The stall-injection build (liblowm_stress.so) must give the same bits.
+
+The TensorRT-LLM PR "Fix two synchronization gaps in the MiniMax M3 low-M
+split-K GEMM" (Hardware verification) found its ordering defects by stalling
+chosen warps for 2 to 100 us, because a missing wait only shows when one
+participant falls far behind.  The stress build stalls chosen wavefronts,
+ranks and tiles with a bounded s_sleep loop at five sites:
+  entry       before the first load (reorders which rank arrives last),
+  stage read  after the stage barrier, before reading an LDS stage (a refill
+              that did not wait for every reader would overwrite it),
+  reduce      before a wavefront hands its sums to the wavefront reduction,
+  publish     before a rank stores its partial and arrives,
+  fold        in the owner, after the acquire, before reading the partials.
+Every stalled launch must equal the unstalled launch of the default build
+with the same tactic bit for bit (same kernels, same summation order), and so
+stay within the oracle's bounds.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_bf16_gemm_amd as sbg
+import workloads
+from checks import assert_bf16
+from gpu_util import device, inputs, oracle_result, say, to_bits
+from split_bf16_gemm_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+DELAYS_NS = (2_000, 5_000, 10_000, 100_000)
+
+# (sites, rank, wave, tile_mod, tile_sel, step)
+PLANS = [
+    ("entry rank 0", binding.SITE_ENTRY, 0, -1, 0, 0, -1),
+    ("entry rank 1, every 3rd tile", binding.SITE_ENTRY, 1, -1, 3, 1, -1),
+    ("stage read wave 1, every step", binding.SITE_STAGE_READ, -1, 1, 0, 0, -1),
+    ("stage read wave 3, step 0", binding.SITE_STAGE_READ, -1, 3, 0, 0, 0),
+    ("reduce wave 2", binding.SITE_REDUCE, -1, 2, 0, 0, -1),
+    ("publish rank 0", binding.SITE_PUBLISH, 0, -1, 0, 0, -1),
+    ("publish rank 1, odd tiles", binding.SITE_PUBLISH, 1, -1, 2, 1, -1),
+    ("fold", binding.SITE_FOLD, -1, -1, 0, 0, -1),
+    ("publish + fold, every 5th tile", binding.SITE_PUBLISH | binding.SITE_FOLD, -1, -1, 5, 2, -1),
+]
+
+TACTICS = [None, binding.tactic("lds", 16, 2, 4), binding.tactic("lds", 16, 2, 3)]
+
+
+@pytest.fixture(scope="module")
+def libs():
+    device()
+    stress = sbg.load("stress")
+    yield sbg.load(), stress
+    stress.configure_stress(0)
+
+
+def launch(lib, ops, wl, tactic):
+    A, W, ws = ops
+    out = lib.gemm(A, W, wl.split_k, workspace=ws, tactic=tactic)
+    torch.cuda.synchronize()
+    return to_bits(out)
+
+
+@pytest.mark.parametrize("tactic", TACTICS, ids=["default", "lds_u2_ns4", "lds_u2_ns3"])
+@pytest.mark.parametrize("plan", PLANS, ids=[p[0] for p in PLANS])
+def test_headline_under_stalls(libs, plan, tactic):
+    base, stress = libs
+    wl = workloads.HEADLINE
+    dev = device()
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    ops = (A, W, ws)
+    say("stress reference", plan[0], tactic)
+    ref = launch(base, ops, wl, tactic)
+    C, S = oracle_result(wl)
+    assert_bf16(ref, C, S, wl.K, oracle.default())
+    name, sites, rank, wave, tmod, tsel, step = plan
+    for d in DELAYS_NS:
+        say("stress", name, d, "ns", tactic)
+        stress.configure_stress(sites, rank, wave, tmod, tsel, step, d)
+        try:
+            got = launch(stress, ops, wl, tactic)
+        finally:
+            stress.configure_stress(0)
+        assert np.array_equal(got, ref), f"{name}, {d} ns: output differs from the unstalled run"
+    assert not ws[:sbg.counter_bytes(wl.N)].cpu().numpy().any()
+
+
+@pytest.mark.parametrize("wl", workloads.sweep(), ids=lambda w: w.name)
+def test_sweep_in_stress_build(libs, wl):
+    base, stress = libs
+    dev = device()
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    ops = (A, W, ws)
+    say("sweep reference", wl.name)
+    ref = launch(base, ops, wl, None)
+    C, S = oracle_result(wl)
+    assert_bf16(ref, C, S, wl.K, oracle.default(), what=wl.name)
+    for sites, rank, wave, d in [(binding.SITE_PUBLISH, 0, -1, 10_000),
+                                 (binding.SITE_ENTRY | binding.SITE_FOLD, -1, 0, 5_000),
+                                 (binding.SITE_REDUCE, -1, 1, 2_000)]:
+        say("sweep stress", wl.name, sites, rank, wave, d)
+        stress.configure_stress(sites, rank, wave, 3, 0, -1, d)
+        try:
+            got = launch(stress, ops, wl, None)
+        finally:
+            stress.configure_stress(0)
+        assert np.array_equal(got, ref), f"{wl.name}: stalls at {sites} changed the output"
+
+
+def test_stress_library_without_stalls_matches(libs):
+    base, stress = libs
+    wl = workloads.SPLITK4
+    dev = device()
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    say("stress lib, no stalls")
+    assert np.array_equal(launch(base, (A, W, ws), wl, None), launch(stress, (A, W, ws), wl, None))
