@@ -106,18 +106,28 @@ int lowm_last_hip_error(void);
  * sweeps and for tests that cover every variant.  Any tactic gives a correct
  * result; the summation order (and so the low bits of random-input results)
  * depends on it.
- *   stage      LOWM_STAGE_LDS: W goes global -> LDS ring of `stages` stages
- *              shared by the workgroup (direct-to-LDS loads), barrier before a
- *              stage is refilled; LOWM_STAGE_REG: W goes global -> registers,
- *              double-buffered per wavefront.
+ *   stage      LOWM_STAGE_LDS: W goes global -> an LDS ring of `stages`
+ *              stages shared by the workgroup; a stage holds 512 K of each of
+ *              the tile's rows, each direct-to-LDS load moving 1 KB of one row;
+ *              a stage is refilled only after a workgroup barrier that every
+ *              wavefront reaches once its reads of it are done.  unroll must
+ *              be 4.  LOWM_STAGE_REG: W goes global -> registers, a ring of
+ *              `stages` register stages per wavefront, `unroll` 32-wide K
+ *              chunks per wavefront per stage; each wavefront streams its
+ *              own contiguous quarter of the K slice.
+ *              LOWM_STAGE_WAVE: a workgroup is one wavefront that owns its
+ *              tile for the whole K slice; W goes global -> a ring of `stages`
+ *              register stages of `unroll` chunks; no barriers at all.
  *   rows       W rows (output columns) per workgroup tile: 16, 32 or 64.
- *   waves      wavefronts per workgroup: 4 (the K slice of a rank is split
- *              between them and their sums are added in wave order).
- *   unroll     32-wide K chunks each wavefront takes per step: 1, 2 or 4.
- *   stages     LDS ring depth for LOWM_STAGE_LDS: 2, 3 or 4.
+ *   waves      wavefronts per workgroup: 4 for LDS and REG (the K slice of a
+ *              rank is split between them and their sums are added in wave
+ *              order), 1 for WAVE.
+ *   unroll     see stage.
+ *   stages     ring depth: 2, 3 or 4 (LDS), 2, 3 or 4 (REG), 2 or 4 (WAVE).
  */
 #define LOWM_STAGE_LDS 0
 #define LOWM_STAGE_REG 1
+#define LOWM_STAGE_WAVE 2
 typedef struct lowm_tactic {
     int stage;
     int rows;

@@ -21,6 +21,7 @@ LOWM_ERR_WORKSPACE = -3
 LOWM_ERR_LAUNCH = -4
 LOWM_STAGE_LDS = 0
 LOWM_STAGE_REG = 1
+LOWM_STAGE_WAVE = 2
 MAX_M = 64
 MAX_SPLIT_K = 256
 
@@ -40,14 +41,17 @@ class Tactic(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
     def __repr__(self) -> str:
-        st = "lds" if self.stage == LOWM_STAGE_LDS else "reg"
+        st = {LOWM_STAGE_LDS: "lds", LOWM_STAGE_REG: "reg", LOWM_STAGE_WAVE: "wave"}.get(
+            self.stage, str(self.stage))
         return (f"Tactic({st}, rows={self.rows}, waves={self.waves}, "
                 f"unroll={self.unroll}, stages={self.stages})")
 
 
-def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 4) -> Tactic:
-    return Tactic(LOWM_STAGE_LDS if stage == "lds" else LOWM_STAGE_REG, rows, waves,
-                  unroll, stages)
+def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 0) -> Tactic:
+    code = {"lds": LOWM_STAGE_LDS, "reg": LOWM_STAGE_REG, "wave": LOWM_STAGE_WAVE}[stage]
+    if waves == 0:
+        waves = 1 if code == LOWM_STAGE_WAVE else 4
+    return Tactic(code, rows, waves, unroll, stages)
 
 
 class LowmError(RuntimeError):
@@ -97,6 +101,8 @@ class Library:
         if self.has_stress:
             lib.lowm_stress_configure.argtypes = [ctypes.c_uint, _i, _i, _i, _i, _i, ctypes.c_uint]
             lib.lowm_stress_configure.restype = _i
+            lib.lowm_stress_trace.argtypes = [_vp]
+            lib.lowm_stress_trace.restype = _i
         self.lib = lib
 
     # -- host-only queries ------------------------------------------------
@@ -169,6 +175,13 @@ class Library:
         if n == 0:
             return None
         return torch.zeros(n, dtype=torch.uint8, device=device)
+
+    def trace(self, buf: Optional[torch.Tensor]):
+        """Stress build: per-workgroup timestamps into ``buf`` (int64 device
+        tensor, 8 per workgroup), or stop tracing with None."""
+        if not self.has_stress:
+            raise RuntimeError(f"{self.path.name} is not a stress build")
+        self.check(self.lib.lowm_stress_trace(None if buf is None else buf.data_ptr()))
 
     def configure_stress(self, sites: int = 0, rank: int = -1, wave: int = -1,
                          tile_mod: int = 0, tile_sel: int = 0, step: int = -1,

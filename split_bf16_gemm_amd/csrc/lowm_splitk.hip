@@ -58,11 +58,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;        // lanes per wavefront
 constexpr int kWaves = 4;        // wavefronts per workgroup
 constexpr int kThreads = kWaves * kWave;
-constexpr int kChunkK = 32;      // K of one MFMA 16x16x32
 constexpr int kVecK = 8;         // bf16 per 16-byte vector
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 
-enum Stage : int { kStageLds = LOWM_STAGE_LDS, kStageReg = LOWM_STAGE_REG };
+enum Stage : int {
+  kStageLds = LOWM_STAGE_LDS,
+  kStageReg = LOWM_STAGE_REG,
+  kStageWave = LOWM_STAGE_WAVE
+};
 
 // ---------------------------------------------------------------------------
 // Stress instrumentation (compiled only with -DLOWM_STRESS)
@@ -83,6 +86,14 @@ struct StressArgs {
   int tile_sel;
   int step;               // kSiteStageRead: only this step (-1: every step)
   uint32_t ticks;         // stall length in s_memrealtime ticks (100 MHz)
+  uint64_t* trace;        // optional per-workgroup timestamps (kTraceSlots each)
+};
+
+// Timestamp trace of the stress build: per workgroup, s_memrealtime (100 MHz)
+// at these points, then the hardware ids of the CU and XCD it ran on.
+enum TraceSlot : int {
+  kTraceEntry = 0, kTraceFirstStage = 1, kTraceLoopEnd = 2, kTraceReduced = 3,
+  kTraceArrived = 4, kTraceEnd = 5, kTraceHwId = 6, kTraceXccId = 7, kTraceSlots = 8
 };
 
 struct Args {
@@ -93,8 +104,6 @@ struct Args {
   float* part;            // [tiles][S][M*BN] fp32 partials
   int M, N, K, S;
   int nvec;               // 16-byte vectors per rank slice: K / S / 8
-  int nchunks;            // MFMA chunks per rank slice: ceil(nvec / 4)
-  int nsteps;             // pipeline steps per rank slice
   int tiles;              // ceil(N / BN)
   StressArgs stress;
 };
@@ -115,8 +124,25 @@ __device__ __forceinline__ void maybe_stall(const StressArgs& st, uint32_t site,
   stall_ticks(st.ticks);
 }
 #define LOWM_STALL(site, step) maybe_stall(a.stress, (site), rank, wave, tile, (step))
+#define LOWM_TRACE(slot)                                                              \
+  do {                                                                                \
+    if (a.stress.trace && threadIdx.x == 0)                                           \
+      a.stress.trace[(size_t)blockIdx.x * kTraceSlots + (slot)] =                      \
+          __builtin_amdgcn_s_memrealtime();                                           \
+  } while (0)
+#define LOWM_TRACE_IDS()                                                              \
+  do {                                                                                \
+    if (a.stress.trace && threadIdx.x == 0) {                                         \
+      a.stress.trace[(size_t)blockIdx.x * kTraceSlots + kTraceHwId] =                  \
+          __builtin_amdgcn_s_getreg(4 | (31 << 11));                                  \
+      a.stress.trace[(size_t)blockIdx.x * kTraceSlots + kTraceXccId] =                 \
+          __builtin_amdgcn_s_getreg(20 | (31 << 11));                                 \
+    }                                                                                 \
+  } while (0)
 #else
 #define LOWM_STALL(site, step) ((void)0)
+#define LOWM_TRACE(slot) ((void)0)
+#define LOWM_TRACE_IDS() ((void)0)
 #endif
 
 // ---------------------------------------------------------------------------
@@ -161,38 +187,66 @@ __device__ __forceinline__ __bf16 to_out<__bf16>(float v) {
 
 // Register/LDS budget of a tactic.  Kept in one place so the host picker and
 // the instantiation filter agree.
-template <int MB, int RG, int STAGE, int U, int NS>
+//
+// LDS variant: a stage is BN weight rows x 512 K (1 KB of each row), stored
+// row by row at a pitch of 1040 bytes; each direct-to-LDS instruction moves
+// one 1 KB contiguous piece of one row.  Each wavefront consumes 4 of the
+// stage's 16 MFMA chunks, so U is 4.
+// REG variant: a step is 4*U chunks; wavefront w loads chunks 4j+w.
+// ACT: 1 = the workgroup's activation slice A[0:M, slice] is moved into LDS
+// once (direct-to-LDS, 1 KB pieces) before the W stream starts; 0 = each
+// wavefront loads its activation operands from L2 alongside each W group.
+template <int MB, int RG, int STAGE, int U, int NS, int ACT>
 struct Shape {
   static constexpr int BN = 16 * RG;
+  static constexpr int kPitch = 65;                     // u32x4 per LDS row (1040 B)
   static constexpr int WU = kWaves * U;                 // chunks per step
-  static constexpr int slot_elems = WU * RG * kWave;    // u32x4 per LDS stage
-  static constexpr int group_loads = U * (RG + MB);     // vmem ops per group
+  static constexpr int slot_elems = (STAGE == kStageLds) ? BN * kPitch : 1;
+  static constexpr int red_floats = kWaves * RG * MB * 4 * kWave;
+  // the wavefront reduction reuses stage 0 when it is large enough
+  static constexpr bool red_in_ring = STAGE == kStageLds && slot_elems * 4 >= red_floats;
+  // vector-memory ops of one pipeline group, per wavefront
+  static constexpr int group_loads = ((STAGE == kStageLds) ? BN / kWaves : U * RG) +
+                                     (ACT ? 0 : U * MB);
   static constexpr int lds_bytes = (STAGE == kStageLds ? NS * slot_elems * 16 : 0) +
-                                   kWaves * RG * MB * 4 * kWave * 4;
+                                   (red_in_ring ? 0 : red_floats * 4);
   static constexpr int stage_vgprs =
-      NS * U * 4 * (MB + (STAGE == kStageReg ? RG : 0));
+      NS * U * 4 * ((ACT ? 0 : MB) + (STAGE == kStageReg ? RG : 0));
   static constexpr bool valid =
-      lds_bytes <= 160 * 1024 && stage_vgprs <= 224 &&
-      (STAGE == kStageReg || (NS - 2) * group_loads <= 63) && NS >= 2 && NS <= 4;
+      lds_bytes <= 128 * 1024 && stage_vgprs <= 224 && NS >= 2 && NS <= 4 &&
+      (STAGE == kStageReg || U == 4) && (NS - 1) * group_loads <= 63 && (!ACT || MB <= 2);
 };
+
+template <int N>
+__device__ __forceinline__ void wait_groups(int younger) {
+  // at most `younger` (0..3) groups of N ops may still be outstanding
+  if (younger <= 0) wait_vmcnt<0>();
+  else if (younger == 1) wait_vmcnt<N>();
+  else if (younger == 2) wait_vmcnt<2 * N <= 63 ? 2 * N : 63>();
+  else wait_vmcnt<3 * N <= 63 ? 3 * N : 63>();
+}
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int MB, int RG, int STAGE, int U, int NS, typename OutT>
+template <int MB, int RG, int STAGE, int U, int NS, int ACT, typename OutT>
 __device__ __forceinline__ void kernel_body(const Args& a) {
-  using SH = Shape<MB, RG, STAGE, U, NS>;
+  using SH = Shape<MB, RG, STAGE, U, NS, ACT>;
   constexpr int BN = SH::BN;
-  constexpr int WU = SH::WU;
-  constexpr int kSlot = (STAGE == kStageLds) ? SH::slot_elems : 1;
+  constexpr int kSlot = SH::slot_elems;
+  constexpr int kPitch = SH::kPitch;
+  constexpr int G = SH::group_loads;
+  constexpr bool kLds = STAGE == kStageLds;
 
   // LDS stages are distinct objects so the compiler can tell that a refill of
   // one stage does not alias reads of another and needs no extra wait.
   __shared__ u32x4 ring0[kSlot];
-  __shared__ u32x4 ring1[kSlot];
-  __shared__ u32x4 ring2[(NS > 2) ? kSlot : 1];
-  __shared__ u32x4 ring3[(NS > 3) ? kSlot : 1];
-  __shared__ float red[kWaves][RG][MB][4][kWave];
+  __shared__ u32x4 ring1[kLds ? kSlot : 1];
+  __shared__ u32x4 ring2[(kLds && NS > 2) ? kSlot : 1];
+  __shared__ u32x4 ring3[(kLds && NS > 3) ? kSlot : 1];
+  __shared__ float red_own[SH::red_in_ring ? 1 : SH::red_floats];
+  // activation slice (ACT): M rows of nvec+1 vectors, sized at launch
+  extern __shared__ u32x4 act_lds[];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -205,42 +259,40 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
   const int q = bid / kXcds;
   const int rank = q % a.S;
   const int tile = (q / a.S) * kXcds + (bid % kXcds);
+  LOWM_TRACE(kTraceEntry);
+  LOWM_TRACE_IDS();
   if (tile >= a.tiles) return;
   const int n0 = tile * BN;
   const int Ks = a.nvec * kVecK;
   const size_t k0 = (size_t)rank * Ks;
+  const int nvec = a.nvec;
 
-  // Per-lane operand rows.  Out-of-range rows are clamped to a valid row so
-  // every load stays in bounds; their results are masked (act) or land only
-  // in output columns that are never stored (W).
-  const uint16_t* wrow[RG];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    int n = n0 + 16 * rg + l16;
-    n = n < a.N ? n : a.N - 1;
-    wrow[rg] = a.W + (size_t)n * a.K + k0;
-  }
+  // K order.  LDS variant: each tile starts its slice at a different 512-wide
+  // stage and wraps around, so the workgroups in flight spread over the
+  // columns of W.  REG variant: wavefront w owns the contiguous chunk range
+  // [w*cpw, (w+1)*cpw) of the slice and streams it front to back, so the
+  // loads it issues back to back cover its 16 rows x U*64 contiguous bytes.
+  const int nunits = kLds ? (nvec + 63) / 64 : (nvec + 3) / 4;
+  const int rot = kLds ? (int)(((unsigned)tile * 5u) % (unsigned)nunits) : 0;
+  auto phys = [&](int u) { return u < nunits ? (u + rot < nunits ? u + rot : u + rot - nunits) : -1; };
+  const bool whole = kLds ? (nvec % 64 == 0) : (nvec % 4 == 0);
+  const int cpw = (nunits + kWaves - 1) / kWaves;            // REG: chunks per wavefront
+  const int nsteps = kLds ? nunits : (cpw + U - 1) / U;
+
+  // Activation rows of this lane per 16-row block; rows >= M are clamped to
+  // row 0 and masked to zero.
   const uint16_t* arow[MB];
+  int arow_lds[MB];
   bool a_ok[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
     const int m = 16 * b + l16;
     a_ok[b] = m < a.M;
     arow[b] = a.A + (size_t)(a_ok[b] ? m : 0) * a.K + k0;
+    arow_lds[b] = (a_ok[b] ? m : 0) * (nvec + 1);
   }
-  const int last_off = (a.nvec - 1) * kVecK;
-
-  // Element offset of this lane's vector in chunk c (clamped into the slice).
-  auto vec_off = [&](int c) {
-    const int off = c * kChunkK + g * kVecK;
-    return off < last_off ? off : last_off;
-  };
-  // Chunks a wavefront loads (and, in the register variant, consumes) in step
-  // s: the four wavefronts' j-th loads are adjacent, so together they sweep
-  // 16 rows x 256 contiguous bytes.
-  auto load_chunk = [&](int s, int j) { return s * WU + j * kWaves + wave; };
-  // Chunks a wavefront consumes in step s of the LDS variant.
-  auto lds_chunk = [&](int s, int j) { return s * WU + wave * U + j; };
+  // Element offset of vector v of the slice, clamped into the slice.
+  auto voff = [&](int v) { return (v < nvec ? v : nvec - 1) * kVecK; };
 
   f32x4 acc[RG][MB];
 #pragma unroll
@@ -248,10 +300,29 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
 #pragma unroll
     for (int b = 0; b < MB; ++b) acc[rg][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Register stages: activation operands always, W operands in the register
-  // variant.
-  u32x4 areg[NS][U][MB];
-  u32x4 wreg[(STAGE == kStageReg) ? NS : 1][U][RG];
+  u32x4 areg[ACT ? 1 : NS][U][MB];
+  u32x4 wreg[kLds ? 1 : NS][U][RG];
+
+  // REG variant: this lane's W rows.
+  const uint16_t* wrow[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    int n = n0 + 16 * rg + l16;
+    n = n < a.N ? n : a.N - 1;
+    wrow[rg] = a.W + (size_t)n * a.K + k0;
+  }
+  // LDS variant: the rows this wavefront moves into each stage (rows wave,
+  // wave+4, ...), lane i carrying bytes [16i, 16i+16) of the row's 1 KB.
+  constexpr int kRowsPerWave = BN / kWaves;
+  const uint16_t* drow[kLds ? kRowsPerWave : 1];
+  if constexpr (kLds) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      int n = n0 + wave + kWaves * i;
+      n = n < a.N ? n : a.N - 1;
+      drow[i] = a.W + (size_t)n * a.K + k0;
+    }
+  }
 
   auto slot_ptr = [&](auto slot_c) -> u32x4* {
     constexpr int SL = decltype(slot_c)::value;
@@ -261,37 +332,54 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     else return ring3;
   };
 
-  // Issue the loads of step s into stage slot SL.  Always issued, even past
-  // the last step (addresses clamped), so the number of vector-memory ops
-  // after any group is a compile-time constant.
+  // Vector index (within the slice) of this lane's operand for chunk j of
+  // step s, or -1 past the end of the slice (or of this wavefront's range).
+  auto operand_vec = [&](int s, int j) {
+    if constexpr (kLds) {
+      const int p = phys(s);
+      return p < 0 ? -1 : p * 64 + (wave * U + j) * 4 + g;
+    } else {
+      const int c = s * U + j;
+      const int chunk = wave * cpw + c;
+      return (c < cpw && chunk < nunits) ? chunk * 4 + g : -1;
+    }
+  };
+  // REG variant: where a load past the end of this wavefront's range reads
+  // instead (its own last chunk, just loaded, so it hits in L2).
+  auto load_vec = [&](int s, int j) {
+    const int c = s * U + j;
+    int chunk = wave * cpw + (c < cpw ? c : cpw - 1);
+    chunk = chunk < nunits ? chunk : nunits - 1;
+    return chunk * 4 + g;
+  };
+
+  // Issue the loads of step s (< nsteps) into stage slot SL.
   auto issue = [&](auto slot_c, int s) {
     constexpr int SL = decltype(slot_c)::value;
-    if constexpr (STAGE == kStageLds) {
+    if constexpr (kLds) {
       u32x4* slot = slot_ptr(slot_c);
+      const int off = voff(phys(s) * 64 + lane);
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int cl = j * kWaves + wave;                 // chunk within the step
-        const int off = vec_off(load_chunk(s, j));
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          // lane i's 16 bytes land at base + 16*i
-          __builtin_amdgcn_global_load_lds(
-              wrow[rg] + off,
-              (__attribute__((address_space(3))) void*)(slot + (cl * RG + rg) * kWave), 16, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int off = vec_off(lds_chunk(s, j));
-#pragma unroll
-        for (int b = 0; b < MB; ++b) areg[SL][j][b] = load16(arow[b] + off);
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        // one contiguous 1 KB piece of row (wave + 4i); lane i's 16 bytes
+        // land at base + 16*i
+        __builtin_amdgcn_global_load_lds(
+            drow[i] + off,
+            (__attribute__((address_space(3))) void*)(slot + (wave + kWaves * i) * kPitch), 16,
+            0, 0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const int off = vec_off(load_chunk(s, j));
+        const int off = voff(load_vec(s, j));
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) wreg[SL][j][rg] = load16(wrow[rg] + off);
+      }
+    }
+    if constexpr (!ACT) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int off = voff(kLds ? max(operand_vec(s, j), 0) : load_vec(s, j));
 #pragma unroll
         for (int b = 0; b < MB; ++b) areg[SL][j][b] = load16(arow[b] + off);
       }
@@ -299,45 +387,61 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     pin_issue();
   };
 
-  // Multiply-accumulate step s out of stage slot SL.
-  auto compute = [&](auto slot_c, int s) {
+  // Multiply-accumulate step s out of stage slot SL.  MASK: some operand of
+  // the step may lie outside the slice (ragged K or a step past the end).
+  auto compute_impl = [&](auto slot_c, auto mask_c, int s) {
     constexpr int SL = decltype(slot_c)::value;
-    // Every chunk of the step is whole and inside the slice: no masking.
-    const bool full = (s + 1) * WU * 4 <= a.nvec;
+    constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int c = (STAGE == kStageLds) ? lds_chunk(s, j) : load_chunk(s, j);
-      const bool v_ok = full || (c * 4 + g < a.nvec);
+      const int v = operand_vec(s, j);
+      bool v_ok = true;
+      if constexpr (MASK) v_ok = v >= 0 && v < nvec;
       u32x4 wv[RG];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
-        if constexpr (STAGE == kStageLds) {
+        if constexpr (kLds) {
           const u32x4* slot = slot_ptr(slot_c);
-          wv[rg] = slot[((wave * U + j) * RG + rg) * kWave + lane];
+          wv[rg] = slot[(16 * rg + l16) * kPitch + (wave * U + j) * 4 + g];
         } else {
           wv[rg] = wreg[SL][j][rg];
         }
-        if (!full) wv[rg] = v_ok ? wv[rg] : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (MASK) wv[rg] = v_ok ? wv[rg] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
-        u32x4 av = areg[SL][j][b];
+        u32x4 av;
+        if constexpr (ACT) {
+          av = act_lds[arow_lds[b] + (v_ok ? v : 0)];
+        } else {
+          av = areg[SL][j][b];
+        }
         av = (a_ok[b] && v_ok) ? av : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) acc[rg][b] = mfma(av, wv[rg], acc[rg][b]);
       }
     }
   };
+  auto compute = [&](auto slot_c, int s) {
+    // every operand of the step lies inside the slice: no masking needed
+    const bool full =
+        whole && (kLds ? s < nunits : ((s + 1) * U <= cpw && (wave + 1) * cpw <= nunits));
+    if (full)
+      compute_impl(slot_c, std::false_type{}, s);
+    else
+      compute_impl(slot_c, std::true_type{}, s);
+  };
 
   // One pipeline step: wait for stage s, refill the stage step s-1 used with
-  // step s+NS-1, compute step s.
+  // step s+NS-1 (if there is one), compute step s.
   auto step = [&](auto slot_c, int s) {
     constexpr int SL = decltype(slot_c)::value;
     constexpr int NEXT = (SL + NS - 1) % NS;
-    if constexpr (STAGE == kStageLds) {
-      // Own loads of stage s have landed once at most the NS-2 younger groups
-      // are outstanding ...
-      wait_vmcnt<(NS - 2) * SH::group_loads>();
+    if constexpr (kLds) {
+      // Own loads of stage s have landed once only the younger groups
+      // (at most NS-2, fewer near the end) are outstanding ...
+      const int younger = min(NS - 2, nsteps - 1 - s);
+      wait_groups<G>(younger);
       // ... every wavefront's reads of the previous stage have completed ...
       wait_lgkmcnt0();
       // ... and after the barrier both hold for the whole workgroup, so the
@@ -345,45 +449,84 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
       barrier_keep_loads();
       LOWM_STALL(kSiteStageRead, s);
     }
-    issue(std::integral_constant<int, NEXT>{}, s + NS - 1);
+    if (s == 0) LOWM_TRACE(kTraceFirstStage);
+    if (s + NS - 1 < nsteps) issue(std::integral_constant<int, NEXT>{}, s + NS - 1);
     compute(slot_c, s);
   };
 
   LOWM_STALL(kSiteEntry, 0);
 
-  // Prologue: groups 0 .. NS-2.
-  issue(std::integral_constant<int, 0>{}, 0);
-  if constexpr (NS > 2) issue(std::integral_constant<int, 1>{}, 1);
-  if constexpr (NS > 3) issue(std::integral_constant<int, 2>{}, 2);
+  // ACT: the activation slice goes to LDS first, 1 KB pieces spread over the
+  // wavefronts (every wavefront issues the same number; surplus issues repeat
+  // the last piece into its own place).
+  if constexpr (ACT) {
+    const int ppr = nvec / 64;                      // pieces per row
+    const int total = a.M * ppr;
+    const int per_wave = (total + kWaves - 1) / kWaves;
+    for (int i = 0; i < per_wave; ++i) {
+      int idx = wave + kWaves * i;
+      idx = idx < total ? idx : total - 1;
+      const int m = idx / ppr, p = idx - (idx / ppr) * ppr;
+      __builtin_amdgcn_global_load_lds(
+          a.A + (size_t)m * a.K + k0 + p * 512 + lane * kVecK,
+          (__attribute__((address_space(3))) void*)(act_lds + m * (nvec + 1) + p * 64), 16, 0, 0);
+    }
+  }
 
-  for (int s = 0; s < a.nsteps; s += NS) {
+  // Prologue: groups 0 .. NS-2 (as many as there are steps).
+  issue(std::integral_constant<int, 0>{}, 0);
+  if constexpr (NS > 2) {
+    if (1 < nsteps) issue(std::integral_constant<int, 1>{}, 1);
+  }
+  if constexpr (NS > 3) {
+    if (2 < nsteps) issue(std::integral_constant<int, 2>{}, 2);
+  }
+  if constexpr (ACT && !kLds) {
+    // The register variant has no stage barrier: wait here until the
+    // activation pieces (older than every group) have landed, then make all
+    // wavefronts' pieces visible to all.
+    wait_groups<G>(min(NS - 1, nsteps));
+    wait_lgkmcnt0();
+    barrier_keep_loads();
+  }
+
+  for (int s = 0; s < nsteps; s += NS) {
     step(std::integral_constant<int, 0>{}, s);
-    if (s + 1 >= a.nsteps) break;
+    if (s + 1 >= nsteps) break;
     step(std::integral_constant<int, 1 % NS>{}, s + 1);
     if constexpr (NS > 2) {
-      if (s + 2 >= a.nsteps) break;
+      if (s + 2 >= nsteps) break;
       step(std::integral_constant<int, 2 % NS>{}, s + 2);
     }
     if constexpr (NS > 3) {
-      if (s + 3 >= a.nsteps) break;
+      if (s + 3 >= nsteps) break;
       step(std::integral_constant<int, 3 % NS>{}, s + 3);
     }
   }
-  // No load may still be writing into LDS or registers when the wavefront
-  // moves on (the trailing groups are clamped re-reads of the last chunk).
-  wait_vmcnt0();
+  LOWM_TRACE(kTraceLoopEnd);
 
-  // Wavefront reduction through LDS, added in wavefront order below.
+  // Wavefront reduction through LDS, added in wavefront order below.  In the
+  // LDS variant it reuses stage 0, which every wavefront must have finished
+  // reading first.
+  float* red = SH::red_in_ring ? reinterpret_cast<float*>(ring0) : red_own;
+  if constexpr (SH::red_in_ring) {
+    wait_lgkmcnt0();
+    barrier_keep_loads();
+  }
+  auto red_at = [&](int w, int rg, int b, int i, int ln) -> float& {
+    return red[(((w * RG + rg) * MB + b) * 4 + i) * kWave + ln];
+  };
   LOWM_STALL(kSiteReduce, 0);
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][rg][b][i][lane] = acc[rg][b][i];
+      for (int i = 0; i < 4; ++i) red_at(wave, rg, b, i, lane) = acc[rg][b][i];
   wait_lgkmcnt0();
   barrier_keep_loads();
   if (wave != 0) return;
+  LOWM_TRACE(kTraceReduced);
 
   // Wavefront 0 owns the epilogue.  Output element e of the tile is (m, nl) =
   // (e / BN, e % BN).  The MFMA keeps D[row][col] in lane col + 16*(row/4),
@@ -393,9 +536,9 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     const int m = e / BN, nl = e - (e / BN) * BN;
     const int b = m >> 4, mm = m & 15;
     const int ln = (nl & 15) + 16 * (mm >> 2), rg = nl >> 4, i = mm & 3;
-    float p = red[0][rg][b][i][ln];
+    float p = red_at(0, rg, b, i, ln);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) p += red[w][rg][b][i][ln];
+    for (int w = 1; w < kWaves; ++w) p += red_at(w, rg, b, i, ln);
     return p;
   };
   OutT* C = static_cast<OutT*>(a.C);
@@ -405,43 +548,295 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
       const int m = e / BN, n = n0 + (e - m * BN);
       if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(rank_sum(e));
     }
+    LOWM_TRACE(kTraceEnd);
     return;
   }
 
-  // a4: publish this rank's partial, then arrive.
+  // a4: publish this rank's partial, then arrive.  The partial is written
+  // with device-scope stores (sc1: written through this XCD's L2 to where
+  // every XCD sees it) and the arrival is issued only after all of them are
+  // acknowledged (vmcnt(0)): the release is carried by the stores' own
+  // scope, so no cache-wide write-back is needed.
   LOWM_STALL(kSitePublish, 0);
   float* slots = a.part + (size_t)tile * a.S * E;
-  for (int e = lane; e < E; e += kWave) slots[(size_t)rank * E + e] = rank_sum(e);
-  // Release at agent scope: the partial is written back past this XCD's L2
-  // before the arrival can be observed (buffer_wbl2 + vmcnt(0)).
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  for (int e = lane; e < E; e += kWave)
+    __hip_atomic_store(slots + (size_t)rank * E + e, rank_sum(e), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmcnt0();
+  pin_issue();
   uint32_t before = 0;
   if (lane == 0)
     before = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
-  if (before != (uint32_t)(a.S - 1)) return;   // not the last rank: done
+  LOWM_TRACE(kTraceArrived);
+  if (before != (uint32_t)(a.S - 1)) {   // not the last rank: done
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
 
-  // a5: the owner.  One acquire at agent scope (buffer_inv), then the fold in
-  // rank order with this rank's partial taken from LDS at its own position.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // a5: the owner.  The peers' partials are read with device-scope loads
+  // (sc1), issued only after the arrival count is known, so they observe
+  // every partial whose arrival was counted; no cache-wide invalidate.  The
+  // fold is in rank order with this rank's partial, from LDS, at its own
+  // position.
   LOWM_STALL(kSiteFold, 0);
   for (int e = lane; e < E; e += kWave) {
     const float own = rank_sum(e);
-    float v = (rank == 0) ? own : slots[e];
-    for (int r = 1; r < a.S; ++r) v += (r == rank) ? own : slots[(size_t)r * E + e];
+    float v = (rank == 0)
+                  ? own
+                  : __hip_atomic_load(slots + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int r = 1; r < a.S; ++r)
+      v += (r == rank) ? own
+                       : __hip_atomic_load(slots + (size_t)r * E + e, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     const int m = e / BN, n = n0 + (e - m * BN);
     if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);  // a6
   }
   // The tile's counter is zero again for the next launch.
   if (lane == 0) __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  LOWM_TRACE(kTraceEnd);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront tiles: one wavefront is the whole workgroup and owns a tile of
+// BN = 16*RG weight rows for its entire K slice, so no wavefront waits for
+// another: no LDS stage barrier and no wavefront reduction.  W streams into a
+// ring of NS register stages of U 32-wide chunks (16 B per lane per chunk and
+// row group); the ring is issued unconditionally (past the end of the slice
+// the addresses repeat the slice's last vector and the products are masked),
+// so the loop body has no branches and the compiler's wait counts stay exact.
+// ---------------------------------------------------------------------------
+template <int MB, int RG, int U, int NS, int ACT>
+struct WaveShape {
+  static constexpr int BN = 16 * RG;
+  static constexpr int stage_vgprs = NS * U * 4 * (RG + (ACT ? 0 : MB));
+  static constexpr bool valid = NS >= 2 && NS <= 4 && stage_vgprs <= 256 && (!ACT || MB <= 2);
+};
+
+template <int MB, int RG, int U, int NS, int ACT, typename OutT>
+__device__ __forceinline__ void wave_tile_body(const Args& a) {
+  constexpr int BN = 16 * RG;
+  extern __shared__ u32x4 act_lds[];   // ACT: M rows of nvec+1 vectors
+
+  const int lane = threadIdx.x;
+  const int wave = 0;
+  (void)wave;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+
+  const int bid = blockIdx.x;
+  const int q = bid / kXcds;
+  const int rank = q % a.S;
+  const int tile = (q / a.S) * kXcds + (bid % kXcds);
+  LOWM_TRACE(kTraceEntry);
+  LOWM_TRACE_IDS();
+  if (tile >= a.tiles) return;
+  const int n0 = tile * BN;
+  const int nvec = a.nvec;
+  const size_t k0 = (size_t)rank * nvec * kVecK;
+  const int nchunks = (nvec + 3) / 4;
+  const int rot = (int)(((unsigned)tile * 5u) % (unsigned)nchunks);
+  const bool whole = nvec % 4 == 0;
+  const int nsteps = (nchunks + U - 1) / U;
+
+  const uint16_t* wrow[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    int n = n0 + 16 * rg + l16;
+    n = n < a.N ? n : a.N - 1;
+    wrow[rg] = a.W + (size_t)n * a.K + k0;
+  }
+  const uint16_t* arow[MB];
+  int arow_lds[MB];
+  bool a_ok[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int m = 16 * b + l16;
+    a_ok[b] = m < a.M;
+    arow[b] = a.A + (size_t)(a_ok[b] ? m : 0) * a.K + k0;
+    arow_lds[b] = (a_ok[b] ? m : 0) * (nvec + 1);
+  }
+
+  LOWM_STALL(kSiteEntry, 0);
+  if constexpr (ACT) {
+    // the activation slice to LDS, 1 KB pieces; read back below after the
+    // compiler's wait for these direct-to-LDS loads
+    const int ppr = nvec / 64;
+    const int total = a.M * ppr;
+    for (int idx = 0; idx < total; ++idx) {
+      const int m = idx / ppr, p = idx - (idx / ppr) * ppr;
+      __builtin_amdgcn_global_load_lds(
+          a.A + (size_t)m * a.K + k0 + p * 512 + lane * kVecK,
+          (__attribute__((address_space(3))) void*)(act_lds + m * (nvec + 1) + p * 64), 16, 0, 0);
+    }
+  }
+
+  // chunk c of the slice in this tile's rotated order; -1 past the end
+  auto phys = [&](int c) {
+    return c < nchunks ? (c + rot < nchunks ? c + rot : c + rot - nchunks) : -1;
+  };
+  auto voff = [&](int v) { return (v < nvec ? v : nvec - 1) * kVecK; };
+
+  f32x4 acc[2][RG][MB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[h][rg][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 wreg[NS][U][RG];
+  u32x4 areg[ACT ? 1 : NS][U][MB];
+
+  auto issue = [&](auto slot_c, int s) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = phys(s * U + j);
+      const int off = voff((p < 0 ? nchunks - 1 : p) * 4 + g);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) wreg[SL][j][rg] = load16(wrow[rg] + off);
+      if constexpr (!ACT) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b) areg[SL][j][b] = load16(arow[b] + off);
+      }
+    }
+    pin_issue();
+  };
+
+  auto compute_impl = [&](auto slot_c, auto mask_c, int s) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int p = phys(s * U + j);
+      const int v = p * 4 + g;
+      bool v_ok = true;
+      if constexpr (MASK) v_ok = p >= 0 && v < nvec;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        u32x4 av;
+        if constexpr (ACT) av = act_lds[arow_lds[b] + (v_ok ? v : 0)];
+        else av = areg[SL][j][b];
+        av = (a_ok[b] && v_ok) ? av : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          u32x4 wv = wreg[SL][j][rg];
+          if constexpr (MASK) wv = v_ok ? wv : u32x4{0u, 0u, 0u, 0u};
+          acc[j & 1][rg][b] = mfma(av, wv, acc[j & 1][rg][b]);
+        }
+      }
+    }
+  };
+  auto step = [&](auto slot_c, int s) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr int NEXT = (SL + NS - 1) % NS;
+    issue(std::integral_constant<int, NEXT>{}, s + NS - 1);
+    if (whole && (s + 1) * U <= nchunks)
+      compute_impl(slot_c, std::false_type{}, s);
+    else
+      compute_impl(slot_c, std::true_type{}, s);
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  if constexpr (NS > 2) issue(std::integral_constant<int, 1>{}, 1);
+  if constexpr (NS > 3) issue(std::integral_constant<int, 2>{}, 2);
+  for (int s = 0; s < nsteps; s += NS) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    if constexpr (NS > 2) step(std::integral_constant<int, 2>{}, s + 2);
+    if constexpr (NS > 3) step(std::integral_constant<int, 3>{}, s + 3);
+  }
+  wait_vmcnt0();
+  LOWM_TRACE(kTraceLoopEnd);
+
+  // This lane's sums: block b, register i is D[4g+i][l16] = C[16b+4g+i][n0+16rg+l16].
+  f32x4 sum[RG][MB];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) sum[rg][b] = acc[0][rg][b] + acc[1][rg][b];
+
+  OutT* C = static_cast<OutT*>(a.C);
+  if (a.S == 1) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * b + 4 * g + i, n = n0 + 16 * rg + l16;
+          if (m < a.M && n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(sum[rg][b][i]);
+        }
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
+
+  // a4: publish (device-scope stores, all acknowledged before the arrival)
+  LOWM_STALL(kSitePublish, 0);
+  const int E = a.M * BN;
+  float* slots = a.part + (size_t)tile * a.S * E;
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16;
+        if (m < a.M)
+          __hip_atomic_store(slots + (size_t)rank * E + m * BN + nl, sum[rg][b][i],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  wait_vmcnt0();
+  pin_issue();
+  uint32_t before = 0;
+  if (lane == 0)
+    before = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __builtin_amdgcn_readfirstlane(before);
+  LOWM_TRACE(kTraceArrived);
+  if (before != (uint32_t)(a.S - 1)) {
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
+
+  // a5/a6: the owner folds in rank order (its own partial from registers)
+  LOWM_STALL(kSiteFold, 0);
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16, n = n0 + nl;
+        if (m >= a.M) continue;
+        const float own = sum[rg][b][i];
+        const int e = m * BN + nl;
+        float v = (rank == 0) ? own
+                              : __hip_atomic_load(slots + e, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        for (int r = 1; r < a.S; ++r)
+          v += (r == rank) ? own
+                           : __hip_atomic_load(slots + (size_t)r * E + e, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);
+      }
+  if (lane == 0) __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  LOWM_TRACE(kTraceEnd);
+}
+
+template <int MB, int RG, int U, int NS, int ACT, typename OutT>
+__global__ __launch_bounds__(kWave) void lowm_wave_kernel(Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  wave_tile_body<MB, RG, U, NS, ACT, OutT>(a);
+#endif
 }
 
 // The body uses device-only builtins (direct-to-LDS loads), which the host
 // pass cannot instantiate; it only needs the launch stub there.
-template <int MB, int RG, int STAGE, int U, int NS, typename OutT>
+template <int MB, int RG, int STAGE, int U, int NS, int ACT, typename OutT>
 __global__ __launch_bounds__(kThreads) void lowm_splitk_kernel(Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  kernel_body<MB, RG, STAGE, U, NS, OutT>(a);
+  kernel_body<MB, RG, STAGE, U, NS, ACT, OutT>(a);
 #endif
 }
 
@@ -451,44 +846,67 @@ __global__ __launch_bounds__(kThreads) void lowm_splitk_kernel(Args a) {
 struct Variant {
   int stage, unroll, stages;
 };
-// The register/LDS variants this build provides (any rows in {16,32,64}).
+// The register/LDS variants this build provides.
 constexpr Variant kVariants[] = {
-    {kStageLds, 2, 4}, {kStageLds, 2, 3}, {kStageLds, 4, 3}, {kStageLds, 1, 4},
-    {kStageReg, 2, 4}, {kStageReg, 4, 3}, {kStageReg, 4, 4}, {kStageReg, 2, 3},
+    {kStageLds, 4, 2},  {kStageLds, 4, 3},  {kStageReg, 8, 2},  {kStageReg, 4, 3},
+    {kStageReg, 4, 4},  {kStageReg, 16, 2}, {kStageReg, 4, 2},  {kStageWave, 4, 4},
+    {kStageWave, 8, 2},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 typedef void (*KernelFn)(Args);
 
-template <int MB, int RG, int VI, typename OutT>
+template <int MB, int RG, int VI, int ACT, typename OutT>
 KernelFn kernel_for() {
   constexpr Variant v = kVariants[VI];
-  if constexpr (Shape<MB, RG, v.stage, v.unroll, v.stages>::valid)
-    return lowm_splitk_kernel<MB, RG, v.stage, v.unroll, v.stages, OutT>;
-  else
+  if constexpr (v.stage == kStageWave) {
+    if constexpr (WaveShape<MB, RG, v.unroll, v.stages, ACT>::valid)
+      return lowm_wave_kernel<MB, RG, v.unroll, v.stages, ACT, OutT>;
+    else
+      return nullptr;
+  } else if constexpr (Shape<MB, RG, v.stage, v.unroll, v.stages, ACT>::valid) {
+    return lowm_splitk_kernel<MB, RG, v.stage, v.unroll, v.stages, ACT, OutT>;
+  } else {
     return nullptr;
+  }
 }
 
-template <int MB, int RG, typename OutT, int... VI>
+template <int MB, int RG, int ACT, typename OutT, int... VI>
 void fill_row(KernelFn* row, std::integer_sequence<int, VI...>) {
-  ((row[VI] = kernel_for<MB, RG, VI, OutT>()), ...);
+  ((row[VI] = kernel_for<MB, RG, VI, ACT, OutT>()), ...);
 }
 
-// table[out][MB-1][rg_index][variant]
+// Rows per tile the build provides: 16 * RG for RG in kRowGroups.
+constexpr int kRowGroups[] = {1, 2, 4};
+constexpr int kNumRowGroups = sizeof(kRowGroups) / sizeof(kRowGroups[0]);
+constexpr int rg_index(int rg) {
+  for (int i = 0; i < kNumRowGroups; ++i)
+    if (kRowGroups[i] == rg) return i;
+  return -1;
+}
+
+// table[out][act][MB-1][rg_index][variant]
 struct Table {
-  KernelFn fn[2][4][3][kNumVariants];
+  KernelFn fn[2][2][4][kNumRowGroups][kNumVariants];
 };
 template <typename OutT, int MB, int RG>
 void fill_one(Table& t, int out) {
-  constexpr int ri = RG == 1 ? 0 : RG == 2 ? 1 : 2;
-  fill_row<MB, RG, OutT>(t.fn[out][MB - 1][ri], std::make_integer_sequence<int, kNumVariants>{});
+  constexpr int ri = rg_index(RG);
+  fill_row<MB, RG, 0, OutT>(t.fn[out][0][MB - 1][ri], std::make_integer_sequence<int, kNumVariants>{});
+  fill_row<MB, RG, 1, OutT>(t.fn[out][1][MB - 1][ri], std::make_integer_sequence<int, kNumVariants>{});
+}
+template <typename OutT, int MB>
+void fill_mb(Table& t, int out) {
+  fill_one<OutT, MB, 1>(t, out);
+  fill_one<OutT, MB, 2>(t, out);
+  fill_one<OutT, MB, 4>(t, out);
 }
 template <typename OutT>
 void fill_out(Table& t, int out) {
-  fill_one<OutT, 1, 1>(t, out); fill_one<OutT, 1, 2>(t, out); fill_one<OutT, 1, 4>(t, out);
-  fill_one<OutT, 2, 1>(t, out); fill_one<OutT, 2, 2>(t, out); fill_one<OutT, 2, 4>(t, out);
-  fill_one<OutT, 3, 1>(t, out); fill_one<OutT, 3, 2>(t, out); fill_one<OutT, 3, 4>(t, out);
-  fill_one<OutT, 4, 1>(t, out); fill_one<OutT, 4, 2>(t, out); fill_one<OutT, 4, 4>(t, out);
+  fill_mb<OutT, 1>(t, out);
+  fill_mb<OutT, 2>(t, out);
+  fill_mb<OutT, 3>(t, out);
+  fill_mb<OutT, 4>(t, out);
 }
 const Table& table() {
   static const Table t = [] {
@@ -501,7 +919,7 @@ const Table& table() {
 }
 
 thread_local int g_last_hip_error = 0;
-StressArgs g_stress = {0u, -1, -1, 0, 0, -1, 0u};
+StressArgs g_stress = {0u, -1, -1, 0, 0, -1, 0u, nullptr};
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -513,6 +931,8 @@ int check_sizes(int M, int N, int K, int S) {
 }
 
 size_t counter_bytes(int N) { return round_up((size_t)4 * ((N + 15) / 16), 256); }
+// Every tile width 16*RG divides this, so tiles * BN <= round_up(N, kPartialPad).
+constexpr size_t kPartialPad = 64;
 
 int variant_index(const lowm_tactic& t) {
   for (int i = 0; i < kNumVariants; ++i)
@@ -522,32 +942,57 @@ int variant_index(const lowm_tactic& t) {
   return -1;
 }
 
-int rows_index(int rows) { return rows == 16 ? 0 : rows == 32 ? 1 : rows == 64 ? 2 : -1; }
+int rows_index(int rows) { return rows % 16 == 0 ? rg_index(rows / 16) : -1; }
 
-KernelFn lookup(bool f32out, int M, const lowm_tactic& t) {
-  if (t.waves != kWaves) return nullptr;
+int threads_of(const lowm_tactic& t) { return t.stage == kStageWave ? kWave : kThreads; }
+
+KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t) {
+  if (t.waves != (t.stage == kStageWave ? 1 : kWaves)) return nullptr;
   const int ri = rows_index(t.rows);
   const int vi = variant_index(t);
   if (ri < 0 || vi < 0 || M < 1 || M > LOWM_MAX_M) return nullptr;
-  return table().fn[f32out ? 1 : 0][(M + 15) / 16 - 1][ri][vi];
+  return table().fn[f32out ? 1 : 0][act][(M + 15) / 16 - 1][ri][vi];
 }
 
-// Default tactic: enough weight rows per tile that re-reading the activation
-// slice per tile stays below the weight traffic, and the first variant in a
-// preference list that this build provides for that shape.
+// Largest activation slice staged in LDS (bytes, padding included).
+constexpr size_t kActLdsMax = 48 * 1024;
+size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
+
+// Default tactic.  Tiles of 16 weight rows for M <= 16 and 32 above (two
+// row groups share each activation load).  Register ring: each of the four
+// wavefronts streams cpw = ceil(chunks / 4) contiguous chunks of its slice.
+// Measured on MI355X: when cpw <= 16 the best ring issues the whole range in
+// its first stage (unroll = the smallest power of two >= cpw, 2 stages);
+// for longer ranges a 4-chunk, 2-stage ring beats deeper ones.  Fall back to
+// other rings, then the single-wavefront and LDS variants, when the build has
+// no such instantiation for this M.
 int pick(int M, int N, int K, int S, lowm_tactic* t) {
   const int rc = check_sizes(M, N, K, S);
   if (rc != LOWM_OK) return rc;
-  static const Variant pref[] = {{kStageReg, 4, 3}, {kStageReg, 2, 4}, {kStageReg, 2, 3},
-                                 {kStageLds, 2, 4}, {kStageLds, 1, 4}};
-  t->waves = kWaves;
-  t->rows = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
-  for (const Variant& v : pref) {
+  (void)N;
+  const int nvec = K / S / kVecK;
+  const int cpw = ((nvec + 3) / 4 + kWaves - 1) / kWaves;
+  const int act = (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) ? 1 : 0;
+  int first_unroll = 4;
+  if (cpw <= 16) {
+    while (first_unroll < cpw) first_unroll *= 2;
+  }
+  const Variant first = {kStageReg, first_unroll, 2};
+  static const Variant others[] = {{kStageReg, 4, 2},  {kStageReg, 4, 3},  {kStageReg, 8, 2},
+                                   {kStageWave, 4, 4}, {kStageWave, 8, 2}, {kStageLds, 4, 2},
+                                   {kStageLds, 4, 3}};
+  t->rows = M <= 16 ? 16 : 32;
+  // (the launch stages the activation slice in LDS exactly when `act` is 1)
+  auto provides = [&](const Variant& v) {
     t->stage = v.stage;
     t->unroll = v.unroll;
     t->stages = v.stages;
-    if (lookup(false, M, *t) && lookup(true, M, *t)) return LOWM_OK;
-  }
+    t->waves = v.stage == kStageWave ? 1 : kWaves;
+    return lookup(false, act, M, *t) && lookup(true, act, M, *t);
+  };
+  if (provides(first)) return LOWM_OK;
+  for (const Variant& v : others)
+    if (provides(v)) return LOWM_OK;
   return LOWM_ERR_UNSUPPORTED;
 }
 
@@ -568,11 +1013,22 @@ int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int
     rc = pick(M, N, K, S, &t);
     if (rc != LOWM_OK) return rc;
   }
-  const KernelFn fn = lookup(f32out, M, t);
+  // Stage the activation slice in LDS when it is small and whole 1 KB
+  // pieces; otherwise the wavefronts load activation operands from L2.
+  const int nvec = K / S / kVecK;
+  KernelFn fn = nullptr;
+  size_t dyn_lds = 0;
+  if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
+    fn = lookup(f32out, 1, M, t);
+    dyn_lds = act_lds_bytes(M, nvec);
+  }
+  if (!fn) {
+    fn = lookup(f32out, 0, M, t);
+    dyn_lds = 0;
+  }
   if (!fn) return LOWM_ERR_UNSUPPORTED;
 
   const int BN = t.rows;
-  const int WU = kWaves * t.unroll;
   Args a;
   a.A = static_cast<const uint16_t*>(A);
   a.W = static_cast<const uint16_t*>(W);
@@ -581,9 +1037,7 @@ int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int
   a.N = N;
   a.K = K;
   a.S = S;
-  a.nvec = K / S / kVecK;
-  a.nchunks = (a.nvec + 3) / 4;
-  a.nsteps = (a.nchunks + WU - 1) / WU;
+  a.nvec = nvec;
   a.tiles = (N + BN - 1) / BN;
   a.ctr = S > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
   a.part = S > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(N))
@@ -595,7 +1049,7 @@ int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int
   if (grid > 0x7fffffffu) return LOWM_ERR_UNSUPPORTED;
   void* kargs[] = {&a};
   hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
-                                   dim3(kThreads), kargs, 0, stream);
+                                   dim3(threads_of(t)), kargs, dyn_lds, stream);
   if (err == hipSuccess) err = hipGetLastError();
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
@@ -639,9 +1093,10 @@ int lowm_gemm_splitk_f32out_ex(const void* A, const void* W, float* C, int M, in
 size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k) {
   if (lowm::check_sizes(M, N, K, split_k) != LOWM_OK || split_k == 1) return 0;
   // counters for up to ceil(N/16) tiles, then [tiles][split_k][M][BN] fp32
-  // partials; tiles * BN never exceeds N rounded up to 64.
+  // partials; tiles * BN never exceeds N rounded up to 64, a multiple of
+  // every tile width.
   return lowm::counter_bytes(N) +
-         (size_t)split_k * (size_t)M * lowm::round_up((size_t)N, 64) * sizeof(float);
+         (size_t)split_k * (size_t)M * lowm::round_up((size_t)N, lowm::kPartialPad) * sizeof(float);
 }
 
 int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out) {
@@ -677,6 +1132,13 @@ int lowm_stress_configure(unsigned site_mask, int rank, int wave, int tile_mod, 
   lowm::g_stress.tile_sel = tile_sel;
   lowm::g_stress.step = step;
   lowm::g_stress.ticks = delay_ns / 10u;  // s_memrealtime: 100 MHz
+  return LOWM_OK;
+}
+
+// Stress build only: record per-workgroup timestamps into `buf` (device
+// memory, 8 uint64 per workgroup of the grid; NULL stops tracing).
+int lowm_stress_trace(void* buf) {
+  lowm::g_stress.trace = static_cast<uint64_t*>(buf);
   return LOWM_OK;
 }
 #endif

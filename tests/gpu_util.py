@@ -40,12 +40,16 @@ def oracle_result(wl: workloads.Workload):
     return oracle.gemm(workloads.bits(A), workloads.bits(W))
 
 
+VARIANTS = [("lds", 4, 2), ("lds", 4, 3),
+            ("reg", 8, 2), ("reg", 4, 3), ("reg", 4, 4), ("reg", 16, 2), ("reg", 4, 2),
+            ("wave", 4, 4), ("wave", 8, 2)]
+
+
 def all_tactics(M: int):
     """Every tactic this build provides for M activation rows."""
     out = []
     for rows in (16, 32, 64):
-        for stage, unroll, stages in [("lds", 2, 4), ("lds", 2, 3), ("lds", 4, 3), ("lds", 1, 4),
-                                      ("reg", 2, 4), ("reg", 4, 3), ("reg", 4, 4), ("reg", 2, 3)]:
+        for stage, unroll, stages in VARIANTS:
             out.append(binding.tactic(stage, rows, unroll, stages))
     return out
 
@@ -70,3 +74,20 @@ def run(lib, A_cpu, W_cpu, split_k, f32out=False, tactic=None, workspace=None, d
         raise
     torch.cuda.synchronize()
     return out.cpu()
+
+
+def assert_bf16_launch(lib, A_dev, W_dev, wl, bits, tactic=None, what=""):
+    """Judge a bf16 output with the rules of tests/checks.py, taking the fp32
+    sibling's output (same kernel and order) for the cancellation rule."""
+    import oracle
+    from checks import assert_bf16, assert_fp32
+    C, S = oracle_result(wl)
+    ws = lib.make_workspace(wl.M, wl.N, wl.K, wl.split_k, A_dev.device)
+    c32 = lib.gemm(A_dev, W_dev, wl.split_k, workspace=ws, tactic=tactic,
+                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    c32 = c32.cpu().numpy()
+    assert_fp32(c32, C, S, what=what)
+    assert np.array_equal(bits, oracle.round_bf16(c32.astype(np.float64))), \
+        f"{what}: bf16 output is not RNE of the fp32 sibling"
+    return assert_bf16(bits, C, S, wl.K, oracle.default(), c32, what=what)

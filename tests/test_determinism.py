@@ -18,8 +18,8 @@ import torch
 import oracle
 import split_bf16_gemm_amd as sbg
 import workloads
-from checks import assert_bf16, assert_fp32
-from gpu_util import device, inputs, oracle_result, say, to_bits
+from checks import assert_fp32
+from gpu_util import assert_bf16_launch, device, inputs, oracle_result, say, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -56,8 +56,7 @@ def test_twenty_launches_bitwise(wl, poison):
         assert np.array_equal(bits[i], bits[i % 2]), f"launch {i} differs from launch {i % 2}"
     assert not np.array_equal(bits[0], bits[1])
     for j, s in enumerate(sets):
-        C, S = oracle_result(s)
-        assert_bf16(bits[j], C, S, s.K, oracle.default(), what=f"{s.name} launch {j}")
+        assert_bf16_launch(lib, *ops[j], s, bits[j], what=f"{s.name} launch {j}")
     ctr = ws[:sbg.counter_bytes(wl.N)].cpu().numpy()
     assert not ctr.any()
 

@@ -120,7 +120,7 @@ def test_every_tactic_random(lib):
     for t in all_tactics(wl.M):
         if check_random(lib, wl, tactic=t, what=repr(t)) is not None:
             ran += 1
-    assert ran >= 8
+    assert ran >= 7
 
 
 def test_every_tactic_small_m_ragged_k(lib):

@@ -21,11 +21,9 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import split_bf16_gemm_amd as sbg
 import workloads
-from checks import assert_bf16
-from gpu_util import device, inputs, oracle_result, say, to_bits
+from gpu_util import assert_bf16_launch, device, inputs, oracle_result, say, to_bits
 from split_bf16_gemm_amd import binding
 
 pytestmark = pytest.mark.gpu
@@ -45,7 +43,8 @@ PLANS = [
     ("publish + fold, every 5th tile", binding.SITE_PUBLISH | binding.SITE_FOLD, -1, -1, 5, 2, -1),
 ]
 
-TACTICS = [None, binding.tactic("lds", 16, 2, 4), binding.tactic("lds", 16, 2, 3)]
+TACTICS = [None, binding.tactic("lds", 16, 4, 2), binding.tactic("reg", 16, 4, 3),
+           binding.tactic("wave", 16, 4, 4)]
 
 
 @pytest.fixture(scope="module")
@@ -63,7 +62,7 @@ def launch(lib, ops, wl, tactic):
     return to_bits(out)
 
 
-@pytest.mark.parametrize("tactic", TACTICS, ids=["default", "lds_u2_ns4", "lds_u2_ns3"])
+@pytest.mark.parametrize("tactic", TACTICS, ids=["default", "lds_ns2", "reg_u4_ns3", "wave_u4_ns4"])
 @pytest.mark.parametrize("plan", PLANS, ids=[p[0] for p in PLANS])
 def test_headline_under_stalls(libs, plan, tactic):
     base, stress = libs
@@ -74,8 +73,7 @@ def test_headline_under_stalls(libs, plan, tactic):
     ops = (A, W, ws)
     say("stress reference", plan[0], tactic)
     ref = launch(base, ops, wl, tactic)
-    C, S = oracle_result(wl)
-    assert_bf16(ref, C, S, wl.K, oracle.default())
+    assert_bf16_launch(base, A, W, wl, ref, tactic=tactic, what="unstalled")
     name, sites, rank, wave, tmod, tsel, step = plan
     for d in DELAYS_NS:
         say("stress", name, d, "ns", tactic)
@@ -97,8 +95,7 @@ def test_sweep_in_stress_build(libs, wl):
     ops = (A, W, ws)
     say("sweep reference", wl.name)
     ref = launch(base, ops, wl, None)
-    C, S = oracle_result(wl)
-    assert_bf16(ref, C, S, wl.K, oracle.default(), what=wl.name)
+    assert_bf16_launch(base, A, W, wl, ref, what=wl.name)
     for sites, rank, wave, d in [(binding.SITE_PUBLISH, 0, -1, 10_000),
                                  (binding.SITE_ENTRY | binding.SITE_FOLD, -1, 0, 5_000),
                                  (binding.SITE_REDUCE, -1, 1, 2_000)]:
