@@ -140,6 +140,12 @@ typedef struct lowm_tactic {
  * Returns LOWM_OK or an error code for sizes it would reject. */
 int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out);
 
+/* Host-only: LOWM_OK if a launch with these sizes, output type (f32out != 0:
+ * fp32) and tactic (NULL: the default) would find a kernel in this build, else
+ * the error code the launch would return for them.  No HIP call is made. */
+int lowm_check_launch(int M, int N, int K, int split_k, int f32out,
+                      const lowm_tactic* tactic);
+
 /* lowm_gemm_splitk / _f32out with an explicit tactic (NULL: the default).
  * LOWM_ERR_UNSUPPORTED for a tactic this build does not provide. */
 int lowm_gemm_splitk_ex(const void* A, const void* W, void* C,

@@ -97,6 +97,8 @@ class Library:
         lib.lowm_last_hip_error.restype = _i
         lib.lowm_pick_tactic.argtypes = [_i, _i, _i, _i, _TP]
         lib.lowm_pick_tactic.restype = _i
+        lib.lowm_check_launch.argtypes = [_i, _i, _i, _i, _i, _TP]
+        lib.lowm_check_launch.restype = _i
         self.has_stress = hasattr(lib, "lowm_stress_configure")
         if self.has_stress:
             lib.lowm_stress_configure.argtypes = [ctypes.c_uint, _i, _i, _i, _i, _i, ctypes.c_uint]
@@ -116,6 +118,12 @@ class Library:
         t = Tactic()
         self.check(self.lib.lowm_pick_tactic(M, N, K, split_k, ctypes.byref(t)))
         return t
+
+    def check_launch(self, M: int, N: int, K: int, split_k: int, f32out: bool = False,
+                     tactic: Optional[Tactic] = None) -> int:
+        """Host-only: the code a launch would return before running (0 = runs)."""
+        return self.lib.lowm_check_launch(M, N, K, split_k, int(f32out),
+                                          None if tactic is None else ctypes.byref(tactic))
 
     def check(self, rc: int):
         if rc != LOWM_OK:

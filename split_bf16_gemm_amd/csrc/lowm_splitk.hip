@@ -185,6 +185,44 @@ __device__ __forceinline__ __bf16 to_out<__bf16>(float v) {
   return static_cast<__bf16>(v);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 
+// ---------------------------------------------------------------------------
+// split-K fold helpers
+// ---------------------------------------------------------------------------
+// Device-scope (sc1) load of a peer's partial.
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The owner's value of one output element: the S rank partials of this tile
+// (slot r at slots[r * E + e]) added in rank order 0..S-1, with this rank's
+// own partial `own` at its own position.  The peers' loads are all issued
+// before the first add so they overlap instead of following one another.
+template <int SN>
+__device__ __forceinline__ float fold_ranks_n(const float* slots, size_t E, int e, int rank,
+                                              float own) {
+  float p[SN];
+#pragma unroll
+  for (int r = 0; r < SN; ++r) p[r] = (r == rank) ? own : load_partial(slots + (size_t)r * E + e);
+  float v = p[0];
+#pragma unroll
+  for (int r = 1; r < SN; ++r) v += p[r];
+  return v;
+}
+
+__device__ __forceinline__ float fold_ranks(const float* slots, size_t E, int e, int S,
+                                            int rank, float own) {
+  switch (S) {
+    case 2: return fold_ranks_n<2>(slots, E, e, rank, own);
+    case 3: return fold_ranks_n<3>(slots, E, e, rank, own);
+    case 4: return fold_ranks_n<4>(slots, E, e, rank, own);
+    case 8: return fold_ranks_n<8>(slots, E, e, rank, own);
+    default: break;
+  }
+  float v = (rank == 0) ? own : load_partial(slots + e);
+  for (int r = 1; r < S; ++r) v += (r == rank) ? own : load_partial(slots + (size_t)r * E + e);
+  return v;
+}
+
 // Register/LDS budget of a tactic.  Kept in one place so the host picker and
 // the instantiation filter agree.
 //
@@ -454,6 +492,10 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     compute(slot_c, s);
   };
 
+  // The arrival counter starts at zero before any wavefront can reach the
+  // end: set here, published by the first barrier every variant executes
+  // (the stage barrier, the activation barrier, or the one below).
+
   LOWM_STALL(kSiteEntry, 0);
 
   // ACT: the activation slice goes to LDS first, 1 KB pieces spread over the
@@ -523,14 +565,18 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red_at(wave, rg, b, i, lane) = acc[rg][b][i];
+  // Every wavefront's sums are in LDS after the barrier; wavefront 0 carries
+  // on alone.  (A variant where the last wavefront to arrive at an LDS
+  // counter carried on, with no barrier, measured slower.)
   wait_lgkmcnt0();
   barrier_keep_loads();
   if (wave != 0) return;
   LOWM_TRACE(kTraceReduced);
 
-  // Wavefront 0 owns the epilogue.  Output element e of the tile is (m, nl) =
-  // (e / BN, e % BN).  The MFMA keeps D[row][col] in lane col + 16*(row/4),
-  // register row % 4; rows are activation rows, columns weight rows.
+  // Wavefront 0 owns the epilogue.  Output element e of the tile is
+  // (m, nl) = (e / BN, e % BN).  The MFMA keeps D[row][col] in lane
+  // col + 16*(row/4), register row % 4; rows are activation rows, columns
+  // weight rows.
   const int E = a.M * BN;
   auto rank_sum = [&](int e) {
     const int m = e / BN, nl = e - (e / BN) * BN;
@@ -581,14 +627,7 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
   // position.
   LOWM_STALL(kSiteFold, 0);
   for (int e = lane; e < E; e += kWave) {
-    const float own = rank_sum(e);
-    float v = (rank == 0)
-                  ? own
-                  : __hip_atomic_load(slots + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int r = 1; r < a.S; ++r)
-      v += (r == rank) ? own
-                       : __hip_atomic_load(slots + (size_t)r * E + e, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+    const float v = fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
     const int m = e / BN, n = n0 + (e - m * BN);
     if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);  // a6
   }
@@ -809,15 +848,7 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16, n = n0 + nl;
         if (m >= a.M) continue;
-        const float own = sum[rg][b][i];
-        const int e = m * BN + nl;
-        float v = (rank == 0) ? own
-                              : __hip_atomic_load(slots + e, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        for (int r = 1; r < a.S; ++r)
-          v += (r == rank) ? own
-                           : __hip_atomic_load(slots + (size_t)r * E + e, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+        const float v = fold_ranks(slots, E, m * BN + nl, a.S, rank, sum[rg][b][i]);
         if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);
       }
   if (lane == 0) __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -982,18 +1013,38 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
                                    {kStageWave, 4, 4}, {kStageWave, 8, 2}, {kStageLds, 4, 2},
                                    {kStageLds, 4, 3}};
   t->rows = M <= 16 ? 16 : 32;
-  // (the launch stages the activation slice in LDS exactly when `act` is 1)
+  // The launch stages the activation slice in LDS when `act` is 1 and the
+  // build has that instantiation, else it loads activation operands from L2;
+  // the tactic must exist in the mode the launch will use.
   auto provides = [&](const Variant& v) {
     t->stage = v.stage;
     t->unroll = v.unroll;
     t->stages = v.stages;
     t->waves = v.stage == kStageWave ? 1 : kWaves;
-    return lookup(false, act, M, *t) && lookup(true, act, M, *t);
+    for (int f = 0; f < 2; ++f) {
+      const bool f32 = f == 1;
+      if (!(act && lookup(f32, 1, M, *t)) && !lookup(f32, 0, M, *t)) return false;
+    }
+    return true;
   };
   if (provides(first)) return LOWM_OK;
   for (const Variant& v : others)
     if (provides(v)) return LOWM_OK;
   return LOWM_ERR_UNSUPPORTED;
+}
+
+// The kernel a launch with tactic t runs: the activation slice is staged in
+// LDS when it is small and whole 1 KB pieces (and the build has that
+// instantiation); otherwise the wavefronts load activation operands from L2.
+KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_t* dyn_lds) {
+  if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
+    if (KernelFn fn = lookup(f32out, 1, M, t)) {
+      *dyn_lds = act_lds_bytes(M, nvec);
+      return fn;
+    }
+  }
+  *dyn_lds = 0;
+  return lookup(f32out, 0, M, t);
 }
 
 int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int K, int S,
@@ -1013,19 +1064,9 @@ int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int
     rc = pick(M, N, K, S, &t);
     if (rc != LOWM_OK) return rc;
   }
-  // Stage the activation slice in LDS when it is small and whole 1 KB
-  // pieces; otherwise the wavefronts load activation operands from L2.
   const int nvec = K / S / kVecK;
-  KernelFn fn = nullptr;
   size_t dyn_lds = 0;
-  if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
-    fn = lookup(f32out, 1, M, t);
-    dyn_lds = act_lds_bytes(M, nvec);
-  }
-  if (!fn) {
-    fn = lookup(f32out, 0, M, t);
-    dyn_lds = 0;
-  }
+  const KernelFn fn = select_kernel(f32out, M, nvec, t, &dyn_lds);
   if (!fn) return LOWM_ERR_UNSUPPORTED;
 
   const int BN = t.rows;
@@ -1097,6 +1138,22 @@ size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k) {
   // every tile width.
   return lowm::counter_bytes(N) +
          (size_t)split_k * (size_t)M * lowm::round_up((size_t)N, lowm::kPartialPad) * sizeof(float);
+}
+
+int lowm_check_launch(int M, int N, int K, int split_k, int f32out, const lowm_tactic* tactic) {
+  int rc = lowm::check_sizes(M, N, K, split_k);
+  if (rc != LOWM_OK) return rc;
+  lowm_tactic t;
+  if (tactic) {
+    t = *tactic;
+  } else {
+    rc = lowm::pick(M, N, K, split_k, &t);
+    if (rc != LOWM_OK) return rc;
+  }
+  size_t dyn = 0;
+  return lowm::select_kernel(f32out != 0, M, K / split_k / lowm::kVecK, t, &dyn)
+             ? LOWM_OK
+             : LOWM_ERR_UNSUPPORTED;
 }
 
 int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out) {

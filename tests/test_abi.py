@@ -140,3 +140,26 @@ def test_pick_tactic_rejects_bad_sizes(lib):
     assert lib.lib.lowm_pick_tactic(65, 64, 256, 1, ctypes.byref(t)) == binding.LOWM_ERR_UNSUPPORTED
     assert lib.lib.lowm_pick_tactic(4, 64, 256, 0, ctypes.byref(t)) == binding.LOWM_ERR_INVALID_ARG
     assert lib.lib.lowm_pick_tactic(4, 64, 256, 1, None) == binding.LOWM_ERR_INVALID_ARG
+
+
+def test_default_tactic_is_launchable_for_every_shape(lib):
+    # every M 1..64 with several K/split_k mixes: the default tactic must have
+    # an instantiation in both output types (the launch must not refuse it)
+    failures = []
+    for M in range(1, 65):
+        for (K, S) in [(512, 1), (512, 2), (1024, 8), (4096, 1), (4096, 2), (4096, 4),
+                       (4096, 8), (12288, 4), (1032, 3), (96, 4), (8, 1), (64, 8)]:
+            for f32 in (False, True):
+                rc = lib.check_launch(M, 97, K, S, f32)
+                if rc != 0:
+                    failures.append((M, K, S, f32, rc))
+    assert not failures, failures[:10]
+
+
+def test_check_launch_reports_validation_errors(lib):
+    assert lib.check_launch(0, 64, 256, 1) == binding.LOWM_ERR_INVALID_ARG
+    assert lib.check_launch(65, 64, 256, 1) == binding.LOWM_ERR_UNSUPPORTED
+    assert lib.check_launch(4, 64, 260, 2) == binding.LOWM_ERR_UNSUPPORTED
+    assert lib.check_launch(4, 64, 256, 2, tactic=binding.tactic("reg", 80, 4, 3)) == \
+        binding.LOWM_ERR_UNSUPPORTED
+    assert lib.check_launch(4, 64, 256, 2) == 0

@@ -265,7 +265,9 @@ def test_fraction_rne_self_check():
 
 
 # --------------------------------------------------------------------------
-# planted mistakes: each must be caught by at least one pin
+# planted mistakes: each must be caught by at least one pin.  The mutants run
+# in this process, so every one of them keeps all accesses inside the
+# buffers the pins pass (a wrong index that left them would corrupt the heap).
 # --------------------------------------------------------------------------
 MUTANTS = {
     "drop_last_k": ("for (int64_t k = 0; k < K; ++k) {\n                acc",
@@ -282,7 +284,7 @@ MUTANTS = {
     "double_rounding": ("uint16_t sign = signbit(x) ? 0x8000u : 0u;",
                         "x = (double)(float)x;\n    uint16_t sign = signbit(x) ? 0x8000u : 0u;"),
     "signed_scale": ("mag += fabs(a[m * K + k]) * fabs(w[k]);", "mag += a[m * K + k] * w[k];"),
-    "column_offset": ("C[m * width + (n - n_begin)] = acc;", "C[m * width + n] = acc;"),
+    "column_order": ("C[m * width + (n - n_begin)] = acc;", "C[m * width + (n_end - 1 - n)] = acc;"),
     "no_overflow": ("if (biased >= 255) return (uint16_t)(sign | 0x7F80u);", ""),
 }
 
