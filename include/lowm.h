@@ -28,7 +28,8 @@
  *
  * Workspace (split_k > 1 only): an opaque device buffer of
  * lowm_gemm_splitk_workspace_bytes(M, N, K, split_k) bytes, 256-byte aligned,
- * holding one arrival counter per output tile followed by the fp32 partials.
+ * holding one arrival counter per output tile, each on its own 256-byte line
+ * (256 * ceil(N / 16) bytes), followed by the fp32 partials.
  * Zero it once before first use (hipMemset).  Every launch that completes
  * leaves all counters at zero again (the owner resets its tile's counter), so
  * the workspace can be reused by the next launch without clearing; the
@@ -88,7 +89,8 @@ int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C,
 
 /*
  * Bytes of workspace a launch with these sizes needs: 0 when split_k == 1,
- * else the counters (rounded up to 256 bytes) plus the fp32 partials.  Returns
+ * else the counters (256 bytes per 16 columns of C) plus the fp32 partials,
+ * split_k * M * round_up(N, 64) floats.  Returns
  * 0 as well for arguments the launch would reject.
  */
 size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k);

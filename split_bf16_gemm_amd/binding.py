@@ -224,8 +224,9 @@ def make_workspace(M, N, K, split_k, device="cuda"):
 
 
 def counter_bytes(N: int) -> int:
-    """Bytes of the counter region at the start of a workspace (see lowm.h)."""
-    return ((4 * ((N + 15) // 16)) + 255) // 256 * 256
+    """Bytes of the counter region at the start of a workspace: one counter
+    per 16 columns of C, each on its own 256-byte line (lowm.h)."""
+    return 256 * ((N + 15) // 16)
 
 
 class BwProbe:

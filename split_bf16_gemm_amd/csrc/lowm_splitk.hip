@@ -28,11 +28,14 @@
 //    arrival counter with a relaxed atomic.  The rank that sees split_k-1
 //    earlier arrivals is the owner: one acquire fence, then it adds the
 //    partials in rank order 0..split_k-1 (its own from registers, at its own
-//    position), rounds once to bf16 and resets the counter.  Scope matters
-//    (PR, Description item 2: a release and an acquire synchronize only when
-//    each one's scope includes the other thread); the acquire is issued once,
-//    on the owner's path only, never in a polling loop (PR, Description item
-//    2, on the cost of an acquiring wait).  No workgroup waits for another.
+//    position), rounds once to bf16 and resets the counter.  Each counter
+//    sits on its own 256-byte line: device-scope atomics on one line are
+//    serialised where they execute, so tiles do not share lines.  Scope
+//    matters (PR, Description item 2: a release and an acquire synchronize
+//    only when each one's scope includes the other thread); the acquire is
+//    issued once, on the owner's path only, never in a polling loop (PR,
+//    Description item 2, on the cost of an acquiring wait).  No workgroup
+//    waits for another.
 //
 // Built twice from this source: liblowm.so, and liblowm_stress.so with
 // -DLOWM_STRESS, which adds bounded s_sleep stalls at chosen sites, ranks,
@@ -60,6 +63,7 @@ constexpr int kWaves = 4;        // wavefronts per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kVecK = 8;         // bf16 per 16-byte vector
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kCtrStride = 64;   // uint32 words between tile counters (256 bytes)
 
 enum Stage : int {
   kStageLds = LOWM_STAGE_LDS,
@@ -100,7 +104,7 @@ struct Args {
   const uint16_t* A;
   const uint16_t* W;
   void* C;
-  uint32_t* ctr;          // [tiles] arrival counters
+  uint32_t* ctr;          // [tiles] arrival counters, kCtrStride words apart
   float* part;            // [tiles][S][M*BN] fp32 partials
   int M, N, K, S;
   int nvec;               // 16-byte vectors per rank slice: K / S / 8
@@ -612,7 +616,8 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
   pin_issue();
   uint32_t before = 0;
   if (lane == 0)
-    before = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __hip_atomic_fetch_add(a.ctr + (size_t)tile * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
   if (before != (uint32_t)(a.S - 1)) {   // not the last rank: done
@@ -632,7 +637,9 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);  // a6
   }
   // The tile's counter is zero again for the next launch.
-  if (lane == 0) __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0)
+    __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   LOWM_TRACE(kTraceEnd);
 }
 
@@ -698,8 +705,9 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
 
   LOWM_STALL(kSiteEntry, 0);
   if constexpr (ACT) {
-    // the activation slice to LDS, 1 KB pieces; read back below after the
-    // compiler's wait for these direct-to-LDS loads
+    // the activation slice to LDS, 1 KB pieces; read back only after the
+    // explicit wait below the prologue (the compiler does not order a read
+    // of LDS after a direct-to-LDS load that writes it)
     const int ppr = nvec / 64;
     const int total = a.M * ppr;
     for (int idx = 0; idx < total; ++idx) {
@@ -780,6 +788,11 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   issue(std::integral_constant<int, 0>{}, 0);
   if constexpr (NS > 2) issue(std::integral_constant<int, 1>{}, 1);
   if constexpr (NS > 3) issue(std::integral_constant<int, 2>{}, 2);
+  if constexpr (ACT) {
+    // The activation pieces went out before the NS-1 prologue groups: once
+    // at most those groups' loads are outstanding, the pieces are in LDS.
+    wait_vmcnt<(NS - 1) * U * RG>();
+  }
   for (int s = 0; s < nsteps; s += NS) {
     step(std::integral_constant<int, 0>{}, s);
     step(std::integral_constant<int, 1>{}, s + 1);
@@ -830,7 +843,8 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   pin_issue();
   uint32_t before = 0;
   if (lane == 0)
-    before = __hip_atomic_fetch_add(a.ctr + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __hip_atomic_fetch_add(a.ctr + (size_t)tile * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
   if (before != (uint32_t)(a.S - 1)) {
@@ -851,7 +865,9 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
         const float v = fold_ranks(slots, E, m * BN + nl, a.S, rank, sum[rg][b][i]);
         if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);
       }
-  if (lane == 0) __hip_atomic_store(a.ctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0)
+    __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   LOWM_TRACE(kTraceEnd);
 }
 
@@ -961,7 +977,7 @@ int check_sizes(int M, int N, int K, int S) {
   return LOWM_OK;
 }
 
-size_t counter_bytes(int N) { return round_up((size_t)4 * ((N + 15) / 16), 256); }
+size_t counter_bytes(int N) { return (size_t)4 * kCtrStride * ((N + 15) / 16); }
 // Every tile width 16*RG divides this, so tiles * BN <= round_up(N, kPartialPad).
 constexpr size_t kPartialPad = 64;
 

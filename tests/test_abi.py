@@ -64,14 +64,25 @@ def test_strerror_names_every_code(lib):
 
 def test_workspace_bytes(lib):
     assert lib.workspace_bytes(4, 6144, 4096, 1) == 0
-    # counters for ceil(N/16) tiles rounded to 256 B, then S*M*round_up(N, 64) fp32
-    assert lib.workspace_bytes(4, 6144, 4096, 2) == 1536 + 2 * 4 * 6144 * 4
-    assert lib.workspace_bytes(4, 2304, 12288, 4) == 768 + 4 * 4 * 2304 * 4
-    assert lib.workspace_bytes(3, 17, 64, 2) == 256 + 2 * 3 * 64 * 4
+    # a 256-byte line per counter, ceil(N/16) counters, then S*M*round_up(N, 64) fp32
+    assert lib.workspace_bytes(4, 6144, 4096, 2) == 384 * 256 + 2 * 4 * 6144 * 4
+    assert lib.workspace_bytes(4, 2304, 12288, 4) == 144 * 256 + 4 * 4 * 2304 * 4
+    assert lib.workspace_bytes(3, 17, 64, 2) == 2 * 256 + 2 * 3 * 64 * 4
     assert lib.workspace_bytes(4, 512, 1024, 3) == 0          # K % (8*3) != 0
     assert lib.workspace_bytes(65, 512, 1024, 2) == 0         # M > 64
     assert lib.workspace_bytes(0, 512, 1024, 2) == 0
-    assert sbg.counter_bytes(6144) == 1536
+    assert sbg.counter_bytes(6144) == 384 * 256
+    assert sbg.counter_bytes(17) == 2 * 256
+
+
+def test_binding_counter_region_matches_the_library(lib):
+    # the partials start right after the counters: workspace = counters + partials
+    for N in (1, 15, 16, 17, 64, 100, 2304, 6144, 49152):
+        for (M, S) in ((1, 2), (4, 2), (16, 8), (64, 3)):
+            K = 8 * S * 4
+            parts = S * M * ((N + 63) // 64 * 64) * 4
+            assert lib.workspace_bytes(M, N, K, S) == sbg.counter_bytes(N) + parts, (M, N, S)
+            assert sbg.counter_bytes(N) % 256 == 0
 
 
 def test_pick_tactic_is_valid_for_every_workload(lib):
