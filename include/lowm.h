@@ -120,16 +120,25 @@ int lowm_last_hip_error(void);
  *              LOWM_STAGE_WAVE: a workgroup is one wavefront that owns its
  *              tile for the whole K slice; W goes global -> a ring of `stages`
  *              register stages of `unroll` chunks; no barriers at all.
+ *              LOWM_STAGE_LINE: W goes global -> LDS in whole 128-byte lines
+ *              (8 rows x 128 B per direct-to-LDS load, non-temporal); each
+ *              wavefront streams its own quarter of the K slice through a
+ *              ring of `stages` slots of 16 rows x 64 K that only it reads,
+ *              with no barrier in the main loop.  unroll must be 2; the K
+ *              slice must be a multiple of 256 (K / split_k % 256 == 0),
+ *              else the launch returns LOWM_ERR_UNSUPPORTED.
  *   rows       W rows (output columns) per workgroup tile: 16, 32 or 64.
- *   waves      wavefronts per workgroup: 4 for LDS and REG (the K slice of a
+ *   waves      wavefronts per workgroup: 4 for LDS, REG and LINE (the K slice of a
  *              rank is split between them and their sums are added in wave
  *              order), 1 for WAVE.
  *   unroll     see stage.
- *   stages     ring depth: 2, 3 or 4 (LDS), 2, 3 or 4 (REG), 2 or 4 (WAVE).
+ *   stages     ring depth: 2, 3 or 4 (LDS), 2, 3 or 4 (REG), 2 or 4 (WAVE),
+ *              2, 3 or 4 (LINE; rows 16, or 32 with 2 stages).
  */
 #define LOWM_STAGE_LDS 0
 #define LOWM_STAGE_REG 1
 #define LOWM_STAGE_WAVE 2
+#define LOWM_STAGE_LINE 3
 typedef struct lowm_tactic {
     int stage;
     int rows;

@@ -68,7 +68,8 @@ constexpr int kCtrStride = 64;   // uint32 words between tile counters (256 byte
 enum Stage : int {
   kStageLds = LOWM_STAGE_LDS,
   kStageReg = LOWM_STAGE_REG,
-  kStageWave = LOWM_STAGE_WAVE
+  kStageWave = LOWM_STAGE_WAVE,
+  kStageLine = LOWM_STAGE_LINE
 };
 
 // ---------------------------------------------------------------------------
@@ -175,6 +176,54 @@ __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Cache-policy operand of the whole-line direct-to-LDS loads of W: `nt`.
+// Each W byte is read once per launch; with whole-line requests the hint
+// streams faster than the default policy (measured read-only on MI355X in
+// this kernel's geometry: 9.0 vs 9.7 us for 48 MiB).
+constexpr int kStreamAux = 2;
+
+// A 16-byte LDS read the compiler does not see as one.  Used for slots that
+// direct-to-LDS loads fill, which the code orders by explicit waits: left to
+// itself the compiler adds a wait for every outstanding load before some of
+// these reads.  The value is usable only after lds_wait() on it.
+__device__ __forceinline__ u32x4 lds_read_opaque(const u32x4* p) {
+  const uint32_t addr =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4*)p;
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+// 24 wait states after the last MFMA that writes any of `acc` (2 or 4
+// accumulators), before anything reads them.  Reading an MFMA result needs
+// wait states that the compiler inserts itself, but it was seen to omit them
+// on a path that branches from the last MFMA straight to the accumulator
+// reads (the first register then held its value from before the last two
+// MFMAs).  The accumulators are operands, so every MFMA producing them is
+// issued before these no-ops and every read comes after.
+template <int N>
+__device__ __forceinline__ void mfma_settle(f32x4 (&acc)[N]) {
+  if constexpr (N == 1) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]));
+  else if constexpr (N == 2)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]));
+  else if constexpr (N == 4)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+  else static_assert(N == 1 || N == 2 || N == 4, "mfma_settle: 1, 2 or 4 accumulators");
+}
+
+// Waits for every outstanding LDS operation; the values read by
+// lds_read_opaque pass through it, so their uses cannot move above it.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&v)[N]) {
+  if constexpr (N == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]) : : "memory");
+  else if constexpr (N == 2)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]) : : "memory");
+  else if constexpr (N == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])
+                 : : "memory");
+  else static_assert(N == 1 || N == 2 || N == 4, "lds_wait: 1, 2 or 4 values");
+}
+
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -266,6 +315,102 @@ __device__ __forceinline__ void wait_groups(int younger) {
   else if (younger == 1) wait_vmcnt<N>();
   else if (younger == 2) wait_vmcnt<2 * N <= 63 ? 2 * N : 63>();
   else wait_vmcnt<3 * N <= 63 ? 3 * N : 63>();
+}
+
+// ---------------------------------------------------------------------------
+// The epilogue of a workgroup of kWaves wavefronts, each holding its own sums
+// of the tile (acc, MFMA D layout).  The sums are added through LDS in
+// wavefront order; wavefront 0 then stores C (split_k 1), or publishes the
+// rank partial and, as the owner, folds the ranks (split_k > 1).  `red` is
+// room for kWaves*RG*MB*4*64 floats that no wavefront still reads.
+// ---------------------------------------------------------------------------
+template <int MB, int RG, typename OutT>
+__device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&acc)[RG][MB],
+                                                   float* red, int wave, int lane, int tile,
+                                                   int rank, int n0) {
+  constexpr int BN = 16 * RG;
+  auto red_at = [&](int w, int rg, int b, int i, int ln) -> float& {
+    return red[(((w * RG + rg) * MB + b) * 4 + i) * kWave + ln];
+  };
+  LOWM_STALL(kSiteReduce, 0);
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red_at(wave, rg, b, i, lane) = acc[rg][b][i];
+  // Every wavefront's sums are in LDS after the barrier; wavefront 0 carries
+  // on alone.  (A variant where the last wavefront to arrive at an LDS
+  // counter carried on, with no barrier, measured slower.)
+  wait_lgkmcnt0();
+  barrier_keep_loads();
+  if (wave != 0) return;
+  LOWM_TRACE(kTraceReduced);
+
+  // Wavefront 0 owns the epilogue.  Output element e of the tile is
+  // (m, nl) = (e / BN, e % BN).  The MFMA keeps D[row][col] in lane
+  // col + 16*(row/4), register row % 4; rows are activation rows, columns
+  // weight rows.
+  const int E = a.M * BN;
+  auto rank_sum = [&](int e) {
+    const int m = e / BN, nl = e - (e / BN) * BN;
+    const int b = m >> 4, mm = m & 15;
+    const int ln = (nl & 15) + 16 * (mm >> 2), rg = nl >> 4, i = mm & 3;
+    float p = red_at(0, rg, b, i, ln);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) p += red_at(w, rg, b, i, ln);
+    return p;
+  };
+  OutT* C = static_cast<OutT*>(a.C);
+
+  if (a.S == 1) {
+    for (int e = lane; e < E; e += kWave) {
+      const int m = e / BN, n = n0 + (e - m * BN);
+      if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(rank_sum(e));
+    }
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
+
+  // a4: publish this rank's partial, then arrive.  The partial is written
+  // with device-scope stores (sc1: written through this XCD's L2 to where
+  // every XCD sees it) and the arrival is issued only after all of them are
+  // acknowledged (vmcnt(0)): the release is carried by the stores' own
+  // scope, so no cache-wide write-back is needed.
+  LOWM_STALL(kSitePublish, 0);
+  float* slots = a.part + (size_t)tile * a.S * E;
+  for (int e = lane; e < E; e += kWave)
+    __hip_atomic_store(slots + (size_t)rank * E + e, rank_sum(e), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmcnt0();
+  pin_issue();
+  uint32_t before = 0;
+  if (lane == 0)
+    before = __hip_atomic_fetch_add(a.ctr + (size_t)tile * kCtrStride, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  before = __builtin_amdgcn_readfirstlane(before);
+  LOWM_TRACE(kTraceArrived);
+  if (before != (uint32_t)(a.S - 1)) {   // not the last rank: done
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
+
+  // a5: the owner.  The peers' partials are read with device-scope loads
+  // (sc1), issued only after the arrival count is known, so they observe
+  // every partial whose arrival was counted; no cache-wide invalidate.  The
+  // fold is in rank order with this rank's partial, from LDS, at its own
+  // position.
+  LOWM_STALL(kSiteFold, 0);
+  for (int e = lane; e < E; e += kWave) {
+    const float v = fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
+    const int m = e / BN, n = n0 + (e - m * BN);
+    if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);  // a6
+  }
+  // The tile's counter is zero again for the next launch.
+  if (lane == 0)
+    __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  LOWM_TRACE(kTraceEnd);
 }
 
 // ---------------------------------------------------------------------------
@@ -559,88 +704,251 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     wait_lgkmcnt0();
     barrier_keep_loads();
   }
-  auto red_at = [&](int w, int rg, int b, int i, int ln) -> float& {
-    return red[(((w * RG + rg) * MB + b) * 4 + i) * kWave + ln];
-  };
-  LOWM_STALL(kSiteReduce, 0);
+  workgroup_epilogue<MB, RG, OutT>(a, acc, red, wave, lane, tile, rank, n0);
+}
+
+// ---------------------------------------------------------------------------
+// Line-pair tiles: W goes global -> LDS with direct-to-LDS loads in which
+// every request is a whole 128-byte line and carries the non-temporal hint
+// (each W byte is read once).  One load moves 8 rows x 128 B; two of them,
+// a "line pair", hold 16 rows x 64 K, the operands of two MFMA chunks.  Each
+// wavefront streams its own contiguous quarter of the K slice through a ring
+// of R line-pair slots that only it reads, so the main loop has no workgroup
+// barrier: a slot is refilled after the wavefront's own reads of it have
+// completed (lgkmcnt), and read after the loads that fill it have landed
+// (vmcnt) -- both waits explicit, since the compiler does not order reads of
+// LDS after direct-to-LDS loads.  The activation operands go global ->
+// registers with each line pair.
+//
+// LDS layout of a slot: per row group, the two 8-row pieces at a pitch of
+// 1088 B (64 B of padding); within a piece, row q's 128 B line at q*128.
+// Lane 8q+j of a load writes position j of row q and fetches 16-byte piece
+// (j - q/2) mod 8 of that row's line: a rotation that makes the MFMA-layout
+// reads (16 rows at one K offset) fall in distinct LDS banks.
+// ---------------------------------------------------------------------------
+template <int MB, int RG, int R>
+struct LineShape {
+  static constexpr int BN = 16 * RG;
+  static constexpr int kPiecePitch = 68;                 // u32x4 (1088 B)
+  static constexpr int slot_elems = RG * 2 * kPiecePitch;  // one wavefront's slot
+  static constexpr int red_floats = kWaves * RG * MB * 4 * kWave;
+  static constexpr int lds_bytes = kWaves * R * slot_elems * 16 + red_floats * 4;
+  static constexpr int a_vgprs = R * 2 * MB * 4;
+  // vector-memory ops per line pair: 2 W loads per row group, 2 A loads per
+  // activation block
+  static constexpr int pair_loads = 2 * RG + 2 * MB;
+  static constexpr bool valid = R >= 2 && R <= 4 && MB <= 2 && lds_bytes <= 48 * 1024 &&
+                                a_vgprs <= 64 && (R - 1) * pair_loads <= 63;
+};
+
+// The ring slots arrive as distinct restrict-qualified pointers: once the
+// body is inlined they carry alias scopes, from which the compiler sees that
+// a refill of one slot does not alias reads of another, and adds no wait of
+// its own beyond the explicit ones.
+template <int MB, int RG, int R, typename OutT>
+__device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict__ ring0,
+                                               u32x4* __restrict__ ring1,
+                                               u32x4* __restrict__ ring2,
+                                               u32x4* __restrict__ ring3,
+                                               float* __restrict__ red) {
+  using SH = LineShape<MB, RG, R>;
+  constexpr int BN = SH::BN;
+  constexpr int kSlot = SH::slot_elems;
+  constexpr int kPP = SH::kPiecePitch;
+  constexpr int G = SH::pair_loads;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+
+  const int bid = blockIdx.x;
+  const int q = bid / kXcds;
+  const int rank = q % a.S;
+  const int tile = (q / a.S) * kXcds + (bid % kXcds);
+  LOWM_TRACE(kTraceEntry);
+  LOWM_TRACE_IDS();
+  if (tile >= a.tiles) return;
+  const int n0 = tile * BN;
+  const int nvec = a.nvec;
+  // line pairs (64 K each) per wavefront; the launch requires nvec % 32 == 0
+  const int P = nvec / 32;
+  const size_t kw = (size_t)rank * nvec * kVecK + (size_t)wave * P * 64;
+
+  // Activation rows of this lane per 16-row block.  Rows >= M read row 0:
+  // MFMA output rows are independent and rows >= M are never stored, so
+  // their operands need no masking (and the operand registers no select,
+  // which would make the compiler wait for them at the top of the loop).
+  const uint16_t* arow[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    const int m = 16 * b + l16;
+    arow[b] = a.A + (size_t)(m < a.M ? m : 0) * a.K + kw + g * kVecK;
+  }
+  // Load sources: row 8i+qr of row group rg, rotated piece of its line.
+  const int qr = lane >> 3;
+  const int piece = ((lane & 7) - (qr >> 1)) & 7;
+  const uint16_t* wsrc[RG][2];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red_at(wave, rg, b, i, lane) = acc[rg][b][i];
-  // Every wavefront's sums are in LDS after the barrier; wavefront 0 carries
-  // on alone.  (A variant where the last wavefront to arrive at an LDS
-  // counter carried on, with no barrier, measured slower.)
-  wait_lgkmcnt0();
-  barrier_keep_loads();
-  if (wave != 0) return;
-  LOWM_TRACE(kTraceReduced);
-
-  // Wavefront 0 owns the epilogue.  Output element e of the tile is
-  // (m, nl) = (e / BN, e % BN).  The MFMA keeps D[row][col] in lane
-  // col + 16*(row/4), register row % 4; rows are activation rows, columns
-  // weight rows.
-  const int E = a.M * BN;
-  auto rank_sum = [&](int e) {
-    const int m = e / BN, nl = e - (e / BN) * BN;
-    const int b = m >> 4, mm = m & 15;
-    const int ln = (nl & 15) + 16 * (mm >> 2), rg = nl >> 4, i = mm & 3;
-    float p = red_at(0, rg, b, i, ln);
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) p += red_at(w, rg, b, i, ln);
-    return p;
-  };
-  OutT* C = static_cast<OutT*>(a.C);
-
-  if (a.S == 1) {
-    for (int e = lane; e < E; e += kWave) {
-      const int m = e / BN, n = n0 + (e - m * BN);
-      if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(rank_sum(e));
+    for (int i = 0; i < 2; ++i) {
+      int n = n0 + 16 * rg + 8 * i + qr;
+      n = n < a.N ? n : a.N - 1;
+      wsrc[rg][i] = a.W + (size_t)n * a.K + kw + piece * kVecK;
     }
-    LOWM_TRACE(kTraceEnd);
-    return;
-  }
+  // MFMA-layout read offsets within a slot: row l16, piece 4c+g of the line.
+  int rpos[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    rpos[c] = (l16 >> 3) * kPP + (l16 & 7) * 8 + ((4 * c + g + ((l16 & 7) >> 1)) & 7);
 
-  // a4: publish this rank's partial, then arrive.  The partial is written
-  // with device-scope stores (sc1: written through this XCD's L2 to where
-  // every XCD sees it) and the arrival is issued only after all of them are
-  // acknowledged (vmcnt(0)): the release is carried by the stores' own
-  // scope, so no cache-wide write-back is needed.
-  LOWM_STALL(kSitePublish, 0);
-  float* slots = a.part + (size_t)tile * a.S * E;
-  for (int e = lane; e < E; e += kWave)
-    __hip_atomic_store(slots + (size_t)rank * E + e, rank_sum(e), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  wait_vmcnt0();
-  pin_issue();
-  uint32_t before = 0;
-  if (lane == 0)
-    before = __hip_atomic_fetch_add(a.ctr + (size_t)tile * kCtrStride, 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-  before = __builtin_amdgcn_readfirstlane(before);
-  LOWM_TRACE(kTraceArrived);
-  if (before != (uint32_t)(a.S - 1)) {   // not the last rank: done
-    LOWM_TRACE(kTraceEnd);
-    return;
-  }
+  f32x4 acc[RG][MB];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[rg][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 areg[R][2][MB];
 
-  // a5: the owner.  The peers' partials are read with device-scope loads
-  // (sc1), issued only after the arrival count is known, so they observe
-  // every partial whose arrival was counted; no cache-wide invalidate.  The
-  // fold is in rank order with this rank's partial, from LDS, at its own
-  // position.
-  LOWM_STALL(kSiteFold, 0);
-  for (int e = lane; e < E; e += kWave) {
-    const float v = fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
-    const int m = e / BN, n = n0 + (e - m * BN);
-    if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);  // a6
+  auto slot_ptr = [&](auto slot_c) -> u32x4* {
+    constexpr int SL = decltype(slot_c)::value;
+    if constexpr (SL == 0) return ring0 + wave * kSlot;
+    else if constexpr (SL == 1) return ring1 + wave * kSlot;
+    else if constexpr (SL == 2) return ring2 + wave * kSlot;
+    else return ring3 + wave * kSlot;
+  };
+  // Line pair p (< P) into slot SL: 2*RG direct-to-LDS loads, then the
+  // activation operands of its two chunks.
+  auto issue = [&](auto slot_c, int p) {
+    constexpr int SL = decltype(slot_c)::value;
+    u32x4* slot = slot_ptr(slot_c);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(
+            wsrc[rg][i] + (size_t)p * 64,
+            (__attribute__((address_space(3))) void*)(slot + (rg * 2 + i) * kPP), 16, 0,
+            kStreamAux);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < MB; ++b) areg[SL][c][b] = load16(arow[b] + (size_t)p * 64 + c * 32);
+    pin_issue();
+  };
+  // Step p (line pair p) out of slot SL: wait until pair p has landed (at
+  // most YOUNGER pairs issued after it still in flight), read it, multiply,
+  // then refill the slot with pair p+R when REFILL says there is one.
+  auto step = [&](auto slot_c, auto younger_c, int p, bool refill) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr int YOUNGER = decltype(younger_c)::value;
+    const u32x4* slot = slot_ptr(slot_c);
+    wait_vmcnt<YOUNGER * G>();
+    LOWM_STALL(kSiteStageRead, p);
+    if (p == 0) LOWM_TRACE(kTraceFirstStage);
+    // both chunks' W operands (the reads are complete after lds_wait, so the
+    // refill below cannot overwrite them early)
+    u32x4 wv[2 * RG];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) wv[c * RG + rg] = lds_read_opaque(slot + rg * 2 * kPP + rpos[c]);
+    lds_wait(wv);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          acc[rg][b] = mfma(areg[SL][c][b], wv[c * RG + rg], acc[rg][b]);
+    if (refill) issue(slot_c, p + R);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using YR = std::integral_constant<int, R - 1>;
+
+  LOWM_STALL(kSiteEntry, 0);
+  // Steady state: whole ring cycles in which every step refills its slot, so
+  // R pairs are always in flight and each wait count is the same constant.
+  // The first cycle runs before the loop: straight-line code keeps the
+  // compiler's own waits for the activation registers exact.
+  auto cycle = [&](int p) {
+    step(I0{}, YR{}, p, true);
+    step(I1{}, YR{}, p + 1, true);
+    if constexpr (R > 2) step(I2{}, YR{}, p + 2, true);
+    if constexpr (R > 3) step(I3{}, YR{}, p + 3, true);
+  };
+  int p0 = 0;
+  if (P >= 2 * R) {
+    // prologue: the first R pairs, unconditionally
+    issue(I0{}, 0);
+    issue(I1{}, 1);
+    if constexpr (R > 2) issue(I2{}, 2);
+    if constexpr (R > 3) issue(I3{}, 3);
+    cycle(0);
+    for (p0 = R; p0 + 2 * R <= P; p0 += R) cycle(p0);
+  } else {
+    // prologue: as many of the first R pairs as there are
+    issue(I0{}, 0);
+    if (1 < P) issue(I1{}, 1);
+    if constexpr (R > 2) {
+      if (2 < P) issue(I2{}, 2);
+    }
+    if constexpr (R > 3) {
+      if (3 < P) issue(I3{}, 3);
+    }
   }
-  // The tile's counter is zero again for the next launch.
-  if (lane == 0)
-    __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  LOWM_TRACE(kTraceEnd);
+  // Tail: the REM = P - p0 remaining pairs (1 .. 2R-1), all issued or
+  // issued by these steps; one straight-line sequence per REM, so every wait
+  // count and refill is a constant.
+  auto tail_step = [&](auto rem_c, auto i_c) {
+    constexpr int REM = decltype(rem_c)::value;
+    constexpr int I = decltype(i_c)::value;
+    if constexpr (I < REM) {
+      constexpr int YOUNGER = (REM - 1 - I) < (R - 1) ? (REM - 1 - I) : (R - 1);
+      step(std::integral_constant<int, I % R>{}, std::integral_constant<int, YOUNGER>{}, p0 + I,
+           I + R < REM);
+    }
+  };
+  auto tail = [&](auto rem_c) {
+    tail_step(rem_c, I0{});
+    tail_step(rem_c, I1{});
+    tail_step(rem_c, I2{});
+    tail_step(rem_c, I3{});
+    tail_step(rem_c, std::integral_constant<int, 4>{});
+    tail_step(rem_c, std::integral_constant<int, 5>{});
+    tail_step(rem_c, std::integral_constant<int, 6>{});
+  };
+  static_assert(2 * R - 1 <= 7, "tail covers at most 7 pairs");
+  switch (P - p0) {
+    case 1: tail(std::integral_constant<int, 1>{}); break;
+    case 2: tail(std::integral_constant<int, 2>{}); break;
+    case 3: tail(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (2 * R - 1 >= 4) tail(std::integral_constant<int, 4>{}); break;
+    case 5: if constexpr (2 * R - 1 >= 5) tail(std::integral_constant<int, 5>{}); break;
+    case 6: if constexpr (2 * R - 1 >= 6) tail(std::integral_constant<int, 6>{}); break;
+    case 7: if constexpr (2 * R - 1 >= 7) tail(std::integral_constant<int, 7>{}); break;
+    default: break;
+  }
+  mfma_settle(reinterpret_cast<f32x4(&)[RG * MB]>(acc));
+  LOWM_TRACE(kTraceLoopEnd);
+  workgroup_epilogue<MB, RG, OutT>(a, acc, red, wave, lane, tile, rank, n0);
+}
+
+template <int MB, int RG, int R, typename OutT>
+__global__ __launch_bounds__(kThreads) void lowm_line_kernel(Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using SH = LineShape<MB, RG, R>;
+  // one LDS object per ring slot (all wavefronts' copies of that slot)
+  __shared__ u32x4 ring0[kWaves * SH::slot_elems];
+  __shared__ u32x4 ring1[kWaves * SH::slot_elems];
+  __shared__ u32x4 ring2[R > 2 ? kWaves * SH::slot_elems : 1];
+  __shared__ u32x4 ring3[R > 3 ? kWaves * SH::slot_elems : 1];
+  __shared__ float red[SH::red_floats];
+  line_tile_body<MB, RG, R, OutT>(a, ring0, ring1, ring2, ring3, red);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -897,7 +1205,7 @@ struct Variant {
 constexpr Variant kVariants[] = {
     {kStageLds, 4, 2},  {kStageLds, 4, 3},  {kStageReg, 8, 2},  {kStageReg, 4, 3},
     {kStageReg, 4, 4},  {kStageReg, 16, 2}, {kStageReg, 4, 2},  {kStageWave, 4, 4},
-    {kStageWave, 8, 2},
+    {kStageWave, 8, 2}, {kStageLine, 2, 2}, {kStageLine, 2, 3}, {kStageLine, 2, 4},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -906,7 +1214,13 @@ typedef void (*KernelFn)(Args);
 template <int MB, int RG, int VI, int ACT, typename OutT>
 KernelFn kernel_for() {
   constexpr Variant v = kVariants[VI];
-  if constexpr (v.stage == kStageWave) {
+  if constexpr (v.stage == kStageLine) {
+    // no staged activation slice: instantiated for act 0 only
+    if constexpr (ACT == 0 && LineShape<MB, RG, v.stages>::valid)
+      return lowm_line_kernel<MB, RG, v.stages, OutT>;
+    else
+      return nullptr;
+  } else if constexpr (v.stage == kStageWave) {
     if constexpr (WaveShape<MB, RG, v.unroll, v.stages, ACT>::valid)
       return lowm_wave_kernel<MB, RG, v.unroll, v.stages, ACT, OutT>;
     else
@@ -1053,6 +1367,9 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
 // LDS when it is small and whole 1 KB pieces (and the build has that
 // instantiation); otherwise the wavefronts load activation operands from L2.
 KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_t* dyn_lds) {
+  *dyn_lds = 0;
+  // line-pair tiles stream whole 64-K line pairs per wavefront
+  if (t.stage == kStageLine && nvec % 32 != 0) return nullptr;
   if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
     if (KernelFn fn = lookup(f32out, 1, M, t)) {
       *dyn_lds = act_lds_bytes(M, nvec);

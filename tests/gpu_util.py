@@ -42,7 +42,8 @@ def oracle_result(wl: workloads.Workload):
 
 VARIANTS = [("lds", 4, 2), ("lds", 4, 3),
             ("reg", 8, 2), ("reg", 4, 3), ("reg", 4, 4), ("reg", 16, 2), ("reg", 4, 2),
-            ("wave", 4, 4), ("wave", 8, 2)]
+            ("wave", 4, 4), ("wave", 8, 2),
+            ("line", 2, 2), ("line", 2, 3), ("line", 2, 4)]
 
 
 def all_tactics(M: int):

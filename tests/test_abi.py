@@ -167,6 +167,21 @@ def test_default_tactic_is_launchable_for_every_shape(lib):
     assert not failures, failures[:10]
 
 
+def test_line_tactic_needs_whole_line_pairs(lib):
+    t = binding.tactic("line", 16, 2, 4)
+    assert lib.check_launch(4, 6144, 4096, 2, tactic=t) == 0
+    assert lib.check_launch(4, 6144, 4096, 2, True, tactic=t) == 0
+    # K / split_k = 1984: 248 vectors, not a whole number of 64-K line pairs per wavefront
+    assert lib.check_launch(4, 6144, 3968, 2, tactic=t) == binding.LOWM_ERR_UNSUPPORTED
+    # more than two 16-row activation blocks, unroll other than 2, a ring past the LDS budget
+    assert lib.check_launch(40, 6144, 4096, 2, tactic=t) == binding.LOWM_ERR_UNSUPPORTED
+    assert lib.check_launch(4, 6144, 4096, 2, tactic=binding.tactic("line", 16, 4, 4)) == \
+        binding.LOWM_ERR_UNSUPPORTED
+    assert lib.check_launch(4, 6144, 4096, 2, tactic=binding.tactic("line", 64, 2, 2)) == \
+        binding.LOWM_ERR_UNSUPPORTED
+    assert repr(t).startswith("Tactic(line")
+
+
 def test_check_launch_reports_validation_errors(lib):
     assert lib.check_launch(0, 64, 256, 1) == binding.LOWM_ERR_INVALID_ARG
     assert lib.check_launch(65, 64, 256, 1) == binding.LOWM_ERR_UNSUPPORTED
