@@ -150,7 +150,7 @@ def hbm_read_ceiling(pool, dev, reps=5):
     import torch
     from split_bf16_gemm_amd import BwProbe
     bw = BwProbe()
-    blocks = 256 * 8
+    blocks = 1024
     sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
     Ws = [s[1] for s in pool.sets]
     for W in Ws:
@@ -206,6 +206,56 @@ def calibrate_copy(dev, launches):
                       "bytes_written": COPY_BYTES, "launches": launches}), flush=True)
 
 
+def _counter_medians(run_dir: Path, counter: str) -> dict:
+    """Median per-dispatch value of `counter` for every kernel in the
+    rocprofv3 counter-collection CSVs under run_dir: {name: (median, n)}."""
+    import csv
+    vals: dict = {}
+    for f in sorted(run_dir.rglob("*counter_collection.csv")):
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") == counter:
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: (statistics.median(v), len(v)) for k, v in vals.items()}
+
+
+def summarize_pmc(wl_name: str, tactic_text, fetch: Path, write: Path, cfetch: Path,
+                  cwrite: Path) -> dict:
+    """HBM bytes per launch of the GEMM kernel from four rocprofv3 --pmc runs
+    (FETCH_SIZE and WRITE_SIZE of bench.py, then of --calibrate-copy), each
+    scaled by what the counter reads for the copy of COPY_BYTES; written to
+    PMC_FILE with the kernel source hash, workload and tactic it belongs to."""
+    import split_bf16_gemm_amd as sbg
+    import workloads
+    wl = workloads.by_name(wl_name)
+    lib = sbg.load()
+    tactic = parse_tactic(tactic_text)
+    tac = tactic if tactic is not None else lib.pick_tactic(wl.M, wl.N, wl.K, wl.split_k)
+
+    def gemm_value(d, counter):
+        med = {k: v for k, v in _counter_medians(d, counter).items() if "lowm_" in k}
+        name = max(med, key=lambda k: med[k][1])      # the kernel launched most often
+        return name, med[name][0]
+
+    def copy_value(d, counter):
+        med = {k: v for k, v in _counter_medians(d, counter).items() if "copy_kernel" in k}
+        return next(iter(med.values()))[0]
+
+    kernel, f_kib = gemm_value(fetch, "FETCH_SIZE")
+    _, w_kib = gemm_value(write, "WRITE_SIZE")
+    cf_kib, cw_kib = copy_value(cfetch, "FETCH_SIZE"), copy_value(cwrite, "WRITE_SIZE")
+    f_scale, w_scale = COPY_BYTES / (cf_kib * 1024), COPY_BYTES / (cw_kib * 1024)
+    traffic = round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale)
+    rec = {"source_sha": source_hash(), "workload": wl.name, "tactic": tac.as_dict(),
+           "kernel": kernel, "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+           "copy_fetch_kib_per_dispatch": cf_kib, "copy_write_kib_per_dispatch": cw_kib,
+           "copy_bytes": COPY_BYTES, "fetch_scale": round(f_scale, 5),
+           "write_scale": round(w_scale, 5), "traffic_bytes_per_launch": traffic,
+           "algorithmic_bytes_per_launch": algorithmic_bytes(wl.M, wl.N, wl.K, wl.split_k)}
+    PMC_FILE.write_text(json.dumps(rec, indent=1) + "\n")
+    return rec
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The fp64 oracle on the host cores: full products of the workload,
     repeated until about budget_s seconds of CPU work."""
@@ -239,10 +289,19 @@ def main():
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="no GPU: write the HBM traffic record from four rocprofv3 --pmc "
+                         "output directories (FETCH_SIZE, WRITE_SIZE of this bench, then of "
+                         "--calibrate-copy)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy kernel (50,331,648 bytes per launch) so "
                          "profiler byte counters can be scaled against a known size")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        rec = summarize_pmc(args.workload, args.tactic, *(Path(d) for d in args.summarize_pmc))
+        print(json.dumps(rec), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

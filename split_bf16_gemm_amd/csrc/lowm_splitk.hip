@@ -1319,14 +1319,21 @@ KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t) {
 constexpr size_t kActLdsMax = 48 * 1024;
 size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
 
-// Default tactic.  Tiles of 16 weight rows for M <= 16 and 32 above (two
-// row groups share each activation load).  Register ring: each of the four
+// Default tactic.  Where the K slice is whole 64-K line pairs per wavefront
+// (K / split_k % 256 == 0) and M <= 32: line-pair tiles of 16 rows, a ring of
+// 4 slots for M <= 4 with 8..15 pairs per wavefront and of 2 otherwise; not
+// for M > 16 with 16 or more pairs, where the register ring below is faster.
+// Measured on MI355X at N 6144, K 4096, M 1..32, split_k 1..8, and at
+// N 2304 K 12288 split_k 4 and N 49152 K 4096 split_k 2: the line tiles
+// beat the register ring by 3-30 % everywhere else.
+// Otherwise tiles of 16 weight rows for M <= 16 and 32 above (two row
+// groups share each activation load) in a register ring: each of the four
 // wavefronts streams cpw = ceil(chunks / 4) contiguous chunks of its slice.
-// Measured on MI355X: when cpw <= 16 the best ring issues the whole range in
-// its first stage (unroll = the smallest power of two >= cpw, 2 stages);
-// for longer ranges a 4-chunk, 2-stage ring beats deeper ones.  Fall back to
-// other rings, then the single-wavefront and LDS variants, when the build has
-// no such instantiation for this M.
+// When cpw <= 16 the best ring issues the whole range in its first stage
+// (unroll = the smallest power of two >= cpw, 2 stages); for longer ranges a
+// 4-chunk, 2-stage ring beats deeper ones.  Fall back to other rings, then
+// the single-wavefront and LDS variants, when the build has no such
+// instantiation for this M.
 int pick(int M, int N, int K, int S, lowm_tactic* t) {
   const int rc = check_sizes(M, N, K, S);
   if (rc != LOWM_OK) return rc;
@@ -1357,6 +1364,15 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
     }
     return true;
   };
+  if (nvec % 32 == 0 && M <= 32) {
+    const int pairs = nvec / 32;   // line pairs per wavefront
+    if (!(M > 16 && pairs >= 16)) {
+      const int ring = (M <= 4 && pairs >= 8 && pairs < 16) ? 4 : 2;
+      t->rows = 16;
+      if (provides({kStageLine, 2, ring})) return LOWM_OK;
+    }
+  }
+  t->rows = M <= 16 ? 16 : 32;
   if (provides(first)) return LOWM_OK;
   for (const Variant& v : others)
     if (provides(v)) return LOWM_OK;

@@ -90,7 +90,23 @@ def test_pick_tactic_is_valid_for_every_workload(lib):
     for wl in workloads.ALL:
         t = lib.pick_tactic(wl.M, wl.N, wl.K, wl.split_k)
         assert t.rows in (16, 32, 64) and t.waves in (1, 4)
-        assert t.rows >= min(32, 16 * ((wl.M + 15) // 16))
+        if t.stage != binding.LOWM_STAGE_LINE:
+            assert t.rows >= min(32, 16 * ((wl.M + 15) // 16))
+        assert lib.check_launch(wl.M, wl.N, wl.K, wl.split_k, tactic=t) == 0
+
+
+def test_pick_prefers_line_pairs_where_measured_faster(lib):
+    line = binding.LOWM_STAGE_LINE
+    t = lib.pick_tactic(4, 6144, 4096, 2)        # 8 line pairs per wavefront
+    assert (t.stage, t.rows, t.unroll, t.stages) == (line, 16, 2, 4)
+    t = lib.pick_tactic(16, 6144, 4096, 8)       # 2 pairs
+    assert (t.stage, t.stages) == (line, 2)
+    t = lib.pick_tactic(32, 6144, 4096, 1)       # M > 16 with 16 pairs: register ring
+    assert t.stage == binding.LOWM_STAGE_REG
+    t = lib.pick_tactic(4, 97, 1032, 3)          # ragged K slice: register ring
+    assert t.stage != line
+    t = lib.pick_tactic(64, 6144, 4096, 2)       # M > 32: register ring
+    assert t.stage != line
 
 
 def call(lib, A=FAKE, W=FAKE, C=FAKE, M=4, N=64, K=256, S=2, ws=FAKE, f32=False, tac=None):
