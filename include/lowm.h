@@ -151,6 +151,14 @@ typedef struct lowm_tactic {
  * Returns LOWM_OK or an error code for sizes it would reject. */
 int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out);
 
+/* Host-only: a split_k for these sizes (written to *split_k), chosen from a
+ * table of the fastest split_k measured on MI355X over M 4 and 16, N 768 ..
+ * 24576, K 2048 .. 16384 (nearest grid point in log2 N and log2 K; M <= 8
+ * uses the M 4 measurements), reduced to a power of two that K allows.  Any
+ * split_k is correct; this one minimises time per call.  Returns LOWM_OK, or
+ * the error code a launch would return for M, N, K. */
+int lowm_pick_split_k(int M, int N, int K, int* split_k);
+
 /* Host-only: LOWM_OK if a launch with these sizes, output type (f32out != 0:
  * fp32) and tactic (NULL: the default) would find a kernel in this build, else
  * the error code the launch would return for them.  No HIP call is made. */

@@ -7,7 +7,7 @@ slice adds in slice order.  The work runs in the HIP kernels of
 calls them.
 """
 from .binding import (BwProbe, Library, LowmError, Tactic, counter_bytes, gemm, load,
-                      make_workspace, tactic, workspace_bytes)
+                      make_workspace, pick_split_k, tactic, workspace_bytes)
 
 __all__ = ["BwProbe", "Library", "LowmError", "Tactic", "counter_bytes", "gemm", "load",
-           "make_workspace", "tactic", "workspace_bytes"]
+           "make_workspace", "pick_split_k", "tactic", "workspace_bytes"]

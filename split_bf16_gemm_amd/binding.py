@@ -101,6 +101,8 @@ class Library:
         lib.lowm_pick_tactic.restype = _i
         lib.lowm_check_launch.argtypes = [_i, _i, _i, _i, _i, _TP]
         lib.lowm_check_launch.restype = _i
+        lib.lowm_pick_split_k.argtypes = [_i, _i, _i, ctypes.POINTER(_i)]
+        lib.lowm_pick_split_k.restype = _i
         self.has_stress = hasattr(lib, "lowm_stress_configure")
         if self.has_stress:
             lib.lowm_stress_configure.argtypes = [ctypes.c_uint, _i, _i, _i, _i, _i, ctypes.c_uint]
@@ -120,6 +122,12 @@ class Library:
         t = Tactic()
         self.check(self.lib.lowm_pick_tactic(M, N, K, split_k, ctypes.byref(t)))
         return t
+
+    def pick_split_k(self, M: int, N: int, K: int) -> int:
+        """Host-only: the split_k measured fastest for these sizes."""
+        s = _i(0)
+        self.check(self.lib.lowm_pick_split_k(M, N, K, ctypes.byref(s)))
+        return s.value
 
     def check_launch(self, M: int, N: int, K: int, split_k: int, f32out: bool = False,
                      tactic: Optional[Tactic] = None) -> int:
@@ -219,6 +227,10 @@ def gemm(A, W, split_k=1, **kw):
 
 def workspace_bytes(M, N, K, split_k):
     return load().workspace_bytes(M, N, K, split_k)
+
+
+def pick_split_k(M, N, K):
+    return load().pick_split_k(M, N, K)
 
 
 def make_workspace(M, N, K, split_k, device="cuda"):

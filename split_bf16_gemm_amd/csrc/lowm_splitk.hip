@@ -44,6 +44,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -1382,6 +1383,48 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
   return LOWM_ERR_UNSUPPORTED;
 }
 
+// split_k for a shape, from a table of the fastest measured on MI355X (default
+// tactic for each split_k, W streamed from HBM): M 4 and 16, N 768 .. 24576,
+// K 2048 .. 16384, split_k 1, 2, 4, 8.  A shape takes its nearest grid point
+// in log2 N and log2 K; M <= 8 uses the M 4 row, larger M the M 16 row.  On
+// the grid every entry is the fastest split_k; off it, the neighbours were
+// within 10 % of each other's best.  split_k pays when the tiles are few and
+// K is long; for M 16 the larger partials make it pay less often.
+constexpr unsigned char kBestSplit[2][6][4] = {
+    // M <= 8            K: 2048 4096 8192 16384
+    {{1, 8, 8, 8},    // N 768
+     {1, 8, 8, 8},    // N 1536
+     {1, 8, 4, 4},    // N 3072
+     {1, 1, 2, 8},    // N 6144
+     {1, 1, 4, 8},    // N 12288
+     {1, 1, 4, 8}},   // N 24576
+    // M > 8
+    {{1, 4, 8, 4},
+     {1, 1, 8, 8},
+     {1, 1, 1, 4},
+     {1, 1, 2, 4},
+     {1, 1, 1, 1},
+     {1, 1, 1, 1}}};
+
+int nearest_log2_index(double x, double base, int last) {
+  const int i = (int)floor(log2(x / base) + 0.5);
+  return i < 0 ? 0 : (i > last ? last : i);
+}
+
+int pick_split(int M, int N, int K, int* split_k) {
+  if (!split_k) return LOWM_ERR_INVALID_ARG;
+  int rc = check_sizes(M, N, K, 1);
+  if (rc != LOWM_OK) return rc;
+  int S = kBestSplit[M <= 8 ? 0 : 1][nearest_log2_index(N, 768.0, 5)]
+                    [nearest_log2_index(K, 2048.0, 3)];
+  // the largest power of two <= S that K allows (a whole number of 16-byte
+  // vectors per slice), preferring slices that are whole line pairs
+  while (S > 1 && K % (kVecK * S) != 0) S /= 2;
+  while (S > 1 && (K / S) % 256 != 0 && K % 256 == 0) S /= 2;
+  *split_k = S;
+  return LOWM_OK;
+}
+
 // The kernel a launch with tactic t runs: the activation slice is staged in
 // LDS when it is small and whole 1 KB pieces (and the build has that
 // instantiation); otherwise the wavefronts load activation operands from L2.
@@ -1490,6 +1533,10 @@ size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k) {
   // every tile width.
   return lowm::counter_bytes(N) +
          (size_t)split_k * (size_t)M * lowm::round_up((size_t)N, lowm::kPartialPad) * sizeof(float);
+}
+
+int lowm_pick_split_k(int M, int N, int K, int* split_k) {
+  return lowm::pick_split(M, N, K, split_k);
 }
 
 int lowm_check_launch(int M, int N, int K, int split_k, int f32out, const lowm_tactic* tactic) {

@@ -198,6 +198,27 @@ def test_line_tactic_needs_whole_line_pairs(lib):
     assert repr(t).startswith("Tactic(line")
 
 
+def test_pick_split_k(lib):
+    # the measured table at its grid points (MI355X, default tactic per split_k)
+    assert lib.pick_split_k(4, 6144, 4096) == 1
+    assert lib.pick_split_k(4, 6144, 8192) == 2
+    assert lib.pick_split_k(4, 768, 4096) == 8
+    assert lib.pick_split_k(4, 3072, 16384) == 4
+    assert lib.pick_split_k(16, 768, 4096) == 4
+    assert lib.pick_split_k(16, 24576, 16384) == 1
+    # always a split_k the launch accepts
+    for M in (1, 4, 9, 16, 33, 64):
+        for N in (1, 100, 768, 2304, 6144, 100000):
+            for K in (8, 64, 264, 1032, 2048, 4096, 12288, 16384, 65536):
+                S = lib.pick_split_k(M, N, K)
+                assert S >= 1 and (S & (S - 1)) == 0
+                assert lib.check_launch(M, N, K, S) == 0, (M, N, K, S)
+    t = ctypes.c_int(0)
+    assert lib.lib.lowm_pick_split_k(0, 64, 256, ctypes.byref(t)) == binding.LOWM_ERR_INVALID_ARG
+    assert lib.lib.lowm_pick_split_k(65, 64, 256, ctypes.byref(t)) == binding.LOWM_ERR_UNSUPPORTED
+    assert lib.lib.lowm_pick_split_k(4, 64, 256, None) == binding.LOWM_ERR_INVALID_ARG
+
+
 def test_check_launch_reports_validation_errors(lib):
     assert lib.check_launch(0, 64, 256, 1) == binding.LOWM_ERR_INVALID_ARG
     assert lib.check_launch(65, 64, 256, 1) == binding.LOWM_ERR_UNSUPPORTED
