@@ -95,6 +95,36 @@ int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C,
  */
 size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k);
 
+/*
+ * Batched launch: `count` (1 .. LOWM_MAX_BATCH) independent products
+ * C_g = A_g * W_g^T that share M, K, split_k and the bf16 output, in one
+ * kernel launch (one launch gap instead of `count`; the GEMMs' tails
+ * overlap).  Each GEMM is exactly what lowm_gemm_splitk computes for it, with
+ * the same tactic (the default for M, K, split_k), so its output is bitwise
+ * the single call's.  The workspace (split_k > 1) is the concatenation, in
+ * order, of each GEMM's own workspace of lowm_gemm_splitk_workspace_bytes
+ * (M, N_g, K, split_k) bytes; lowm_gemm_splitk_batched_workspace_bytes gives
+ * the total.  Zero it once; every completed launch leaves it reusable.
+ * Errors as lowm_gemm_splitk, checked for every GEMM before any HIP call;
+ * count < 1 or a NULL `gemms` is LOWM_ERR_INVALID_ARG, count > LOWM_MAX_BATCH
+ * LOWM_ERR_UNSUPPORTED.
+ */
+#define LOWM_MAX_BATCH 8
+typedef struct lowm_gemm_desc {
+    const void* A;   /* bf16 [M, K] */
+    const void* W;   /* bf16 [N, K] */
+    void* C;         /* bf16 [M, N] */
+    int N;
+} lowm_gemm_desc;
+
+int lowm_gemm_splitk_batched(const lowm_gemm_desc* gemms, int count, int M, int K,
+                             int split_k, void* workspace, void* stream);
+
+/* Total workspace bytes of a batched launch (0 when split_k == 1, or for
+ * arguments the launch would reject). */
+size_t lowm_gemm_splitk_batched_workspace_bytes(const lowm_gemm_desc* gemms, int count,
+                                                int M, int K, int split_k);
+
 /* Static text naming an error code. */
 const char* lowm_strerror(int code);
 

@@ -6,8 +6,10 @@ slice adds in slice order.  The work runs in the HIP kernels of
 ``_lib/liblowm.so`` (C ABI in ``include/lowm.h``); this package only loads and
 calls them.
 """
-from .binding import (BwProbe, Library, LowmError, Tactic, counter_bytes, gemm, load,
+from .binding import (MAX_BATCH, BwProbe, GemmDesc, Library, LowmError, Tactic,
+                      batched_workspace_bytes, counter_bytes, gemm, gemm_batched, load,
                       make_workspace, pick_split_k, tactic, workspace_bytes)
 
-__all__ = ["BwProbe", "Library", "LowmError", "Tactic", "counter_bytes", "gemm", "load",
+__all__ = ["MAX_BATCH", "BwProbe", "GemmDesc", "Library", "LowmError", "Tactic",
+           "batched_workspace_bytes", "counter_bytes", "gemm", "gemm_batched", "load",
            "make_workspace", "pick_split_k", "tactic", "workspace_bytes"]

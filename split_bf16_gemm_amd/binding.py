@@ -56,6 +56,14 @@ def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 0) -> T
     return Tactic(code, rows, waves, unroll, stages)
 
 
+MAX_BATCH = 8
+
+
+class GemmDesc(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("W", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("N", ctypes.c_int)]
+
+
 class LowmError(RuntimeError):
     def __init__(self, code: int, message: str, hip_error: int = 0):
         super().__init__(f"lowm error {code}: {message}"
@@ -103,6 +111,12 @@ class Library:
         lib.lowm_check_launch.restype = _i
         lib.lowm_pick_split_k.argtypes = [_i, _i, _i, ctypes.POINTER(_i)]
         lib.lowm_pick_split_k.restype = _i
+        lib.lowm_gemm_splitk_batched.argtypes = [ctypes.POINTER(GemmDesc), _i, _i, _i, _i, _vp,
+                                                 _vp]
+        lib.lowm_gemm_splitk_batched.restype = _i
+        lib.lowm_gemm_splitk_batched_workspace_bytes.argtypes = [ctypes.POINTER(GemmDesc), _i,
+                                                                 _i, _i, _i]
+        lib.lowm_gemm_splitk_batched_workspace_bytes.restype = ctypes.c_size_t
         self.has_stress = hasattr(lib, "lowm_stress_configure")
         if self.has_stress:
             lib.lowm_stress_configure.argtypes = [ctypes.c_uint, _i, _i, _i, _i, _i, ctypes.c_uint]
@@ -186,6 +200,50 @@ class Library:
         self.check(rc)
         return out
 
+    @staticmethod
+    def descs(As, Ws, Cs):
+        """A ctypes array of lowm_gemm_desc for lists of GPU tensors."""
+        arr = (GemmDesc * len(Ws))()
+        for g, (A, W, C) in enumerate(zip(As, Ws, Cs)):
+            arr[g] = GemmDesc(A.data_ptr(), W.data_ptr(), C.data_ptr(), W.shape[0])
+        return arr
+
+    def batched_workspace_bytes(self, M: int, Ns, K: int, split_k: int) -> int:
+        """Bytes of a batch's workspace: the single-GEMM workspaces of its
+        GEMMs, back to back in batch order (0 for split_k 1 or a bad batch)."""
+        arr = (GemmDesc * max(1, len(Ns)))()
+        for g, N in enumerate(Ns):
+            arr[g] = GemmDesc(None, None, None, N)
+        return int(self.lib.lowm_gemm_splitk_batched_workspace_bytes(arr, len(Ns), M, K, split_k))
+
+    def gemm_batched(self, As, Ws, split_k: int = 1, outs=None, workspace=None, stream=None):
+        """[A_g @ W_g.T for each g] in one launch (bf16 out).  All A_g share M and
+        K; the W_g share K; up to MAX_BATCH GEMMs."""
+        if len(As) != len(Ws) or not As:
+            raise ValueError("need as many A as W, at least one")
+        M, K = As[0].shape
+        for A, W in zip(As, Ws):
+            if A.shape != (M, K) or W.dim() != 2 or W.shape[1] != K:
+                raise ValueError("every A must be [M, K] and every W [N, K]")
+            if A.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+                raise TypeError("A and W must be bfloat16")
+            if not (A.is_cuda and W.is_cuda and A.is_contiguous() and W.is_contiguous()):
+                raise ValueError("A and W must be contiguous GPU tensors")
+        if outs is None:
+            outs = [torch.empty((M, W.shape[0]), dtype=torch.bfloat16, device=A.device)
+                    for A, W in zip(As, Ws)]
+        ws_ptr = 0
+        if split_k > 1:
+            need = self.batched_workspace_bytes(M, [W.shape[0] for W in Ws], K, split_k)
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                raise ValueError(f"split_k={split_k} needs a zeroed workspace of {need} bytes")
+            ws_ptr = workspace.data_ptr()
+        s = stream if stream is not None else torch.cuda.current_stream(As[0].device)
+        arr = self.descs(As, Ws, outs)
+        self.check(self.lib.lowm_gemm_splitk_batched(arr, len(Ws), M, K, split_k, ws_ptr,
+                                                     s.cuda_stream))
+        return outs
+
     def make_workspace(self, M: int, N: int, K: int, split_k: int,
                        device="cuda") -> Optional[torch.Tensor]:
         """A zeroed workspace for these sizes (None when split_k == 1)."""
@@ -227,6 +285,14 @@ def gemm(A, W, split_k=1, **kw):
 
 def workspace_bytes(M, N, K, split_k):
     return load().workspace_bytes(M, N, K, split_k)
+
+
+def gemm_batched(As, Ws, split_k=1, **kw):
+    return load().gemm_batched(As, Ws, split_k, **kw)
+
+
+def batched_workspace_bytes(M, Ns, K, split_k):
+    return load().batched_workspace_bytes(M, Ns, K, split_k)
 
 
 def pick_split_k(M, N, K):

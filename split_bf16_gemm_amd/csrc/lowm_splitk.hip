@@ -114,8 +114,49 @@ struct Args {
   int M, N, K, S;
   int nvec;               // 16-byte vectors per rank slice: K / S / 8
   int tiles;              // ceil(N / BN)
+  int bid_base;           // first workgroup of this GEMM in a batched launch
   StressArgs stress;
 };
+
+// Batched launch: up to kMaxBatch independent GEMMs with one M, K and split_k
+// in one grid.  GEMM g owns the workgroups [bid_end of g-1, bid_end of g),
+// each range a multiple of 8 so that the ranks of a tile still share an XCD.
+constexpr int kMaxBatch = LOWM_MAX_BATCH;
+struct GemmSlot {
+  const uint16_t* A;
+  const uint16_t* W;
+  void* C;
+  uint32_t* ctr;
+  float* part;
+  int N;
+  int tiles;
+  int bid_end;
+};
+struct Batch {
+  int count;              // 1: Args describes the only GEMM
+  GemmSlot g[kMaxBatch];
+};
+
+// The Args of the GEMM this workgroup belongs to.
+__device__ __forceinline__ Args gemm_args(const Args& a, const Batch& bt) {
+  Args b = a;
+  if (bt.count > 1) {
+    int g = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxBatch - 1; ++i)
+      if (i < bt.count - 1 && (int)blockIdx.x >= bt.g[i].bid_end) g = i + 1;
+    const GemmSlot& s = bt.g[g];
+    b.A = s.A;
+    b.W = s.W;
+    b.C = s.C;
+    b.ctr = s.ctr;
+    b.part = s.part;
+    b.N = s.N;
+    b.tiles = s.tiles;
+    b.bid_base = g > 0 ? bt.g[g - 1].bid_end : 0;
+  }
+  return b;
+}
 
 #ifdef LOWM_STRESS
 __device__ __forceinline__ void stall_ticks(uint32_t ticks) {
@@ -446,7 +487,7 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
 
   // a0: blockIdx -> (tile, rank).  Workgroups are dealt to the 8 XCDs
   // round-robin; the ranks of one tile share blockIdx % 8, hence one XCD.
-  const int bid = blockIdx.x;
+  const int bid = (int)blockIdx.x - a.bid_base;
   const int q = bid / kXcds;
   const int rank = q % a.S;
   const int tile = (q / a.S) * kXcds + (bid % kXcds);
@@ -766,7 +807,7 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
-  const int bid = blockIdx.x;
+  const int bid = (int)blockIdx.x - a.bid_base;
   const int q = bid / kXcds;
   const int rank = q % a.S;
   const int tile = (q / a.S) * kXcds + (bid % kXcds);
@@ -942,8 +983,9 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
 }
 
 template <int MB, int RG, int R, typename OutT>
-__global__ __launch_bounds__(kThreads) void lowm_line_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) void lowm_line_kernel(Args a0, Batch bt) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  const Args a = gemm_args(a0, bt);
   using SH = LineShape<MB, RG, R>;
   // one LDS object per ring slot (all wavefronts' copies of that slot)
   __shared__ u32x4 ring0[kWaves * SH::slot_elems];
@@ -982,7 +1024,7 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
-  const int bid = blockIdx.x;
+  const int bid = (int)blockIdx.x - a.bid_base;
   const int q = bid / kXcds;
   const int rank = q % a.S;
   const int tile = (q / a.S) * kXcds + (bid % kXcds);
@@ -1184,18 +1226,18 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
 }
 
 template <int MB, int RG, int U, int NS, int ACT, typename OutT>
-__global__ __launch_bounds__(kWave) void lowm_wave_kernel(Args a) {
+__global__ __launch_bounds__(kWave) void lowm_wave_kernel(Args a, Batch bt) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  wave_tile_body<MB, RG, U, NS, ACT, OutT>(a);
+  wave_tile_body<MB, RG, U, NS, ACT, OutT>(gemm_args(a, bt));
 #endif
 }
 
 // The body uses device-only builtins (direct-to-LDS loads), which the host
 // pass cannot instantiate; it only needs the launch stub there.
 template <int MB, int RG, int STAGE, int U, int NS, int ACT, typename OutT>
-__global__ __launch_bounds__(kThreads) void lowm_splitk_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) void lowm_splitk_kernel(Args a, Batch bt) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  kernel_body<MB, RG, STAGE, U, NS, ACT, OutT>(a);
+  kernel_body<MB, RG, STAGE, U, NS, ACT, OutT>(gemm_args(a, bt));
 #endif
 }
 
@@ -1213,7 +1255,7 @@ constexpr Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-typedef void (*KernelFn)(Args);
+typedef void (*KernelFn)(Args, Batch);
 
 template <int MB, int RG, int VI, int ACT, typename OutT>
 KernelFn kernel_for() {
@@ -1442,21 +1484,40 @@ KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_
   return lookup(f32out, 0, M, t);
 }
 
-int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int K, int S,
-           void* workspace, hipStream_t stream, const lowm_tactic* tactic) {
-  if (!A || !W || !C) return LOWM_ERR_INVALID_ARG;
-  int rc = check_sizes(M, N, K, S);
-  if (rc != LOWM_OK) return rc;
+size_t workspace_bytes(int M, int N, int K, int S) {
+  if (check_sizes(M, N, K, S) != LOWM_OK || S == 1) return 0;
+  // counters for up to ceil(N/16) tiles, then [tiles][split_k][M][BN] fp32
+  // partials; tiles * BN never exceeds N rounded up to 64, a multiple of
+  // every tile width.  Both parts are multiples of 256 bytes.
+  return counter_bytes(N) + (size_t)S * (size_t)M * round_up((size_t)N, kPartialPad) * sizeof(float);
+}
+
+// One launch of `count` GEMMs sharing M, K, split_k, the output type and the
+// tactic; the single-GEMM entry points are the count == 1 case.  GEMM g's
+// workspace follows GEMM g-1's (each is workspace_bytes of its own sizes).
+int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int K, int S,
+                 void* workspace, hipStream_t stream, const lowm_tactic* tactic) {
+  if (!gemms || count < 1) return LOWM_ERR_INVALID_ARG;
+  if (count > kMaxBatch) return LOWM_ERR_UNSUPPORTED;
+  for (int g = 0; g < count; ++g)
+    if (!gemms[g].A || !gemms[g].W || !gemms[g].C) return LOWM_ERR_INVALID_ARG;
+  int rc = LOWM_OK;
+  for (int g = 0; g < count; ++g) {
+    rc = check_sizes(M, gemms[g].N, K, S);
+    if (rc != LOWM_OK) return rc;
+  }
   if (S > 1 && !workspace) return LOWM_ERR_WORKSPACE;
-  if (((uintptr_t)A | (uintptr_t)W) & 15) return LOWM_ERR_UNSUPPORTED;
-  if ((uintptr_t)C & (f32out ? 3 : 1)) return LOWM_ERR_UNSUPPORTED;
+  for (int g = 0; g < count; ++g) {
+    if (((uintptr_t)gemms[g].A | (uintptr_t)gemms[g].W) & 15) return LOWM_ERR_UNSUPPORTED;
+    if ((uintptr_t)gemms[g].C & (f32out ? 3 : 1)) return LOWM_ERR_UNSUPPORTED;
+  }
   if (S > 1 && ((uintptr_t)workspace & 15)) return LOWM_ERR_UNSUPPORTED;
 
   lowm_tactic t;
   if (tactic) {
     t = *tactic;
   } else {
-    rc = pick(M, N, K, S, &t);
+    rc = pick(M, gemms[0].N, K, S, &t);
     if (rc != LOWM_OK) return rc;
   }
   const int nvec = K / S / kVecK;
@@ -1465,25 +1526,43 @@ int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int
   if (!fn) return LOWM_ERR_UNSUPPORTED;
 
   const int BN = t.rows;
+  Batch bt;
+  bt.count = count;
+  size_t grid = 0, ws_off = 0;
+  for (int g = 0; g < count; ++g) {
+    GemmSlot& sl = bt.g[g];
+    const int N = gemms[g].N;
+    sl.A = static_cast<const uint16_t*>(gemms[g].A);
+    sl.W = static_cast<const uint16_t*>(gemms[g].W);
+    sl.C = gemms[g].C;
+    sl.N = N;
+    sl.tiles = (N + BN - 1) / BN;
+    char* ws = static_cast<char*>(workspace) + ws_off;
+    sl.ctr = S > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+    sl.part = S > 1 ? reinterpret_cast<float*>(ws + counter_bytes(N)) : nullptr;
+    ws_off += workspace_bytes(M, N, K, S);
+    grid += round_up((size_t)sl.tiles, kXcds) * (size_t)S;
+    if (grid > 0x7fffffffu) return LOWM_ERR_UNSUPPORTED;
+    sl.bid_end = (int)grid;
+  }
+  for (int g = count; g < kMaxBatch; ++g) bt.g[g] = bt.g[count - 1];
+
   Args a;
-  a.A = static_cast<const uint16_t*>(A);
-  a.W = static_cast<const uint16_t*>(W);
-  a.C = C;
+  a.A = bt.g[0].A;
+  a.W = bt.g[0].W;
+  a.C = bt.g[0].C;
   a.M = M;
-  a.N = N;
+  a.N = bt.g[0].N;
   a.K = K;
   a.S = S;
   a.nvec = nvec;
-  a.tiles = (N + BN - 1) / BN;
-  a.ctr = S > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
-  a.part = S > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(N))
-                 : nullptr;
+  a.tiles = bt.g[0].tiles;
+  a.ctr = bt.g[0].ctr;
+  a.part = bt.g[0].part;
+  a.bid_base = 0;
   a.stress = g_stress;
 
-  const size_t tiles_pad = round_up((size_t)a.tiles, kXcds);
-  const size_t grid = tiles_pad * (size_t)S;
-  if (grid > 0x7fffffffu) return LOWM_ERR_UNSUPPORTED;
-  void* kargs[] = {&a};
+  void* kargs[] = {&a, &bt};
   hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
                                    dim3(threads_of(t)), kargs, dyn_lds, stream);
   if (err == hipSuccess) err = hipGetLastError();
@@ -1492,6 +1571,12 @@ int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int
     return LOWM_ERR_LAUNCH;
   }
   return LOWM_OK;
+}
+
+int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int K, int S,
+           void* workspace, hipStream_t stream, const lowm_tactic* tactic) {
+  const lowm_gemm_desc one = {A, W, C, N};
+  return launch_batch(&one, 1, f32out, M, K, S, workspace, stream, tactic);
 }
 
 }  // namespace lowm
@@ -1527,12 +1612,24 @@ int lowm_gemm_splitk_f32out_ex(const void* A, const void* W, float* C, int M, in
 }
 
 size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k) {
-  if (lowm::check_sizes(M, N, K, split_k) != LOWM_OK || split_k == 1) return 0;
-  // counters for up to ceil(N/16) tiles, then [tiles][split_k][M][BN] fp32
-  // partials; tiles * BN never exceeds N rounded up to 64, a multiple of
-  // every tile width.
-  return lowm::counter_bytes(N) +
-         (size_t)split_k * (size_t)M * lowm::round_up((size_t)N, lowm::kPartialPad) * sizeof(float);
+  return lowm::workspace_bytes(M, N, K, split_k);
+}
+
+int lowm_gemm_splitk_batched(const lowm_gemm_desc* gemms, int count, int M, int K,
+                             int split_k, void* workspace, void* stream) {
+  return lowm::launch_batch(gemms, count, false, M, K, split_k, workspace,
+                            static_cast<hipStream_t>(stream), nullptr);
+}
+
+size_t lowm_gemm_splitk_batched_workspace_bytes(const lowm_gemm_desc* gemms, int count, int M,
+                                                int K, int split_k) {
+  if (!gemms || count < 1 || count > LOWM_MAX_BATCH) return 0;
+  size_t total = 0;
+  for (int g = 0; g < count; ++g) {
+    if (lowm::check_sizes(M, gemms[g].N, K, split_k) != LOWM_OK) return 0;
+    total += lowm::workspace_bytes(M, gemms[g].N, K, split_k);
+  }
+  return total;
 }
 
 int lowm_pick_split_k(int M, int N, int K, int* split_k) {

@@ -219,6 +219,38 @@ def test_pick_split_k(lib):
     assert lib.lib.lowm_pick_split_k(4, 64, 256, None) == binding.LOWM_ERR_INVALID_ARG
 
 
+def batch_call(lib, descs, count=None, M=4, K=256, S=2, ws=FAKE):
+    n = len(descs) if count is None else count
+    arr = (binding.GemmDesc * max(1, len(descs)))(*descs)
+    return lib.lib.lowm_gemm_splitk_batched(arr if descs else None, n, M, K, S, ws, None)
+
+
+def test_batched_validation(lib):
+    d = binding.GemmDesc(FAKE, FAKE, FAKE, 64)
+    assert batch_call(lib, [], count=0) == binding.LOWM_ERR_INVALID_ARG
+    assert batch_call(lib, [d], count=0) == binding.LOWM_ERR_INVALID_ARG
+    assert batch_call(lib, [d] * 9) == binding.LOWM_ERR_UNSUPPORTED
+    assert batch_call(lib, [d, binding.GemmDesc(FAKE, 0, FAKE, 64)]) == binding.LOWM_ERR_INVALID_ARG
+    assert batch_call(lib, [d, binding.GemmDesc(FAKE, FAKE, FAKE, 0)]) == binding.LOWM_ERR_INVALID_ARG
+    assert batch_call(lib, [d, d], M=65) == binding.LOWM_ERR_UNSUPPORTED
+    assert batch_call(lib, [d, binding.GemmDesc(FAKE, FAKE + 8, FAKE, 64)]) == \
+        binding.LOWM_ERR_UNSUPPORTED
+    assert batch_call(lib, [d, binding.GemmDesc(FAKE, FAKE, FAKE_ODD + 1, 64)]) == \
+        binding.LOWM_ERR_UNSUPPORTED
+    assert batch_call(lib, [d, d], ws=0) == binding.LOWM_ERR_WORKSPACE
+    assert lib.lib.lowm_last_hip_error() == 0
+
+
+def test_batched_workspace_is_the_concatenation(lib):
+    Ns = [6144, 1024, 300]
+    assert lib.batched_workspace_bytes(4, Ns, 4096, 2) == sum(
+        lib.workspace_bytes(4, N, 4096, 2) for N in Ns)
+    assert lib.batched_workspace_bytes(4, Ns, 4096, 1) == 0
+    assert lib.batched_workspace_bytes(4, [64] * 9, 4096, 2) == 0
+    for N in (1, 17, 300, 6144):
+        assert lib.workspace_bytes(4, N, 4096, 2) % 256 == 0
+
+
 def test_check_launch_reports_validation_errors(lib):
     assert lib.check_launch(0, 64, 256, 1) == binding.LOWM_ERR_INVALID_ARG
     assert lib.check_launch(65, 64, 256, 1) == binding.LOWM_ERR_UNSUPPORTED

@@ -1,0 +1,82 @@
+"""Batched launches: several independent GEMMs that share M, K and split_k in
+one kernel launch.  Each GEMM of a batch must equal, bit for bit, the single
+launch of the same product (same kernel, same summation order); the first one
+is also judged against the oracle, and every counter of the workspace must be
+zero again afterwards."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import split_bf16_gemm_amd as sbg
+import workloads
+from gpu_util import assert_bf16_launch, device, inputs, say, to_bits
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (4, [6144, 1024, 1024], 4096, 2),      # a wide projection and two narrow ones
+    (4, [300, 17, 2304, 64], 2048, 4),     # ragged N
+    (20, [512, 640, 96], 2048, 2),         # two activation blocks
+    (4, [1024, 2048], 1024, 1),            # split_k 1: no workspace
+    (1, [6144] * 8, 4096, 8),              # the largest batch
+    (4, [768], 4096, 2),                   # a batch of one
+]
+
+
+def batch_workloads(M, Ns, K, S):
+    return [workloads.Workload(f"batch_m{M}_n{N}_k{K}_s{S}_{g}", M, N, K, S,
+                               seed_a=100 + g, seed_w=200 + g)
+            for g, N in enumerate(Ns)]
+
+
+@pytest.mark.parametrize("M,Ns,K,S", CASES)
+def test_batch_equals_single_launches(M, Ns, K, S):
+    lib = sbg.load()
+    dev = device()
+    wls = batch_workloads(M, Ns, K, S)
+    As = [inputs(wl)[0].to(dev) for wl in wls]
+    Ws = [inputs(wl)[1].to(dev) for wl in wls]
+    ws = None
+    if S > 1:
+        ws = torch.zeros(lib.batched_workspace_bytes(M, Ns, K, S), dtype=torch.uint8,
+                         device=dev)
+    say("batched", M, Ns, K, S)
+    outs = lib.gemm_batched(As, Ws, S, workspace=ws)
+    torch.cuda.synchronize()
+    got = [to_bits(o) for o in outs]
+    for g, wl in enumerate(wls):
+        single = lib.gemm(As[g], Ws[g], S, workspace=lib.make_workspace(M, Ns[g], K, S, dev))
+        torch.cuda.synchronize()
+        assert np.array_equal(got[g], to_bits(single)), \
+            f"GEMM {g} of the batch differs from its single launch"
+    assert_bf16_launch(lib, As[0], Ws[0], wls[0], got[0], what="batch GEMM 0")
+    if ws is not None:
+        off = 0
+        for N in Ns:
+            ctr = ws[off:off + sbg.counter_bytes(N)].cpu().numpy()
+            assert not ctr.any(), "a counter of the batch was left non-zero"
+            off += lib.workspace_bytes(M, N, K, S)
+
+
+def test_batch_reuses_its_workspace():
+    """Two batches in a row on one workspace, the second with other shapes."""
+    lib = sbg.load()
+    dev = device()
+    K, S = 2048, 2
+    first = batch_workloads(4, [2304, 512], K, S)
+    second = batch_workloads(4, [96, 33, 640], K, S)
+    size = max(lib.batched_workspace_bytes(4, [w.N for w in first], K, S),
+               lib.batched_workspace_bytes(4, [w.N for w in second], K, S))
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+    for wls in (first, second):
+        As = [inputs(wl)[0].to(dev) for wl in wls]
+        Ws = [inputs(wl)[1].to(dev) for wl in wls]
+        say("batched reuse", [w.N for w in wls])
+        outs = lib.gemm_batched(As, Ws, S, workspace=ws)
+        torch.cuda.synchronize()
+        for g, wl in enumerate(wls):
+            single = lib.gemm(As[g], Ws[g], S, workspace=lib.make_workspace(4, wl.N, K, S, dev))
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(outs[g]), to_bits(single))
