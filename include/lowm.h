@@ -205,6 +205,52 @@ int lowm_gemm_splitk_f32out_ex(const void* A, const void* W, float* C,
                                void* workspace, void* stream,
                                const lowm_tactic* tactic);
 
+/*
+ * Push epilogue.  The pages name a push epilogue among the shipped variants
+ * of the kernel (split_k 1 and 2, with and without it) and state that only
+ * the owner of an output tile publishes it, without defining it further
+ * (TensorRT-LLM PR "Fix two synchronization gaps in the MiniMax M3 low-M
+ * split-K GEMM", Hardware verification and Test Coverage).  Reading taken
+ * here: the owner of each output tile (the last-arriving rank; every
+ * workgroup when split_k == 1) writes its bf16 tile to C as
+ * lowm_gemm_splitk does and also to a caller-given exchange buffer, for
+ * instance where the next operation of a tensor-parallel layer reads it, and
+ * then raises a flag per 16 output columns so that a consumer can start on
+ * the columns that are ready.
+ *
+ *   push      bf16 exchange buffer: element (m, n) goes to push[m * push_ld + n];
+ *             push_ld >= N elements; 2-byte aligned.
+ *   flags     uint32 [ceil(N / 16)]: flag j covers columns 16j .. 16j+15;
+ *             4-byte aligned.
+ *   flag_value  non-zero value written to each flag.
+ *
+ * The pushed elements are written with system-scope stores and a flag is
+ * written, also at system scope, only after every pushed store of its
+ * columns has been acknowledged: an observer that reads flag j == flag_value
+ * with a system-scope (or, on this device, device-scope) load and then reads
+ * those columns with such loads sees the final values.  The library never
+ * resets the flags: the consumer clears them, or the caller uses a new
+ * flag_value per call.  C, the exchange buffer and the flags must not
+ * overlap (LOWM_ERR_INVALID_ARG).  Output C and all other arguments and
+ * errors are as lowm_gemm_splitk_ex (tactic NULL: the default).
+ */
+int lowm_gemm_splitk_push(const void* A, const void* W, void* C, int M, int N, int K,
+                          int split_k, void* workspace, void* push, int push_ld,
+                          uint32_t* flags, uint32_t flag_value, void* stream,
+                          const lowm_tactic* tactic);
+
+/*
+ * Consumer side of the push epilogue: enqueues on `stream` one wavefront that
+ * polls flags[0 .. n_flags-1] with system-scope loads until each equals
+ * flag_value, or until timeout_us microseconds have passed, and then writes
+ * to the device int *missing the number of flags it did not see set (0: all
+ * were).  Work enqueued after it on `stream` runs after it.  n_flags 1 ..
+ * 4096, timeout_us <= 10,000,000, flag_value non-zero; the wait is bounded
+ * whether or not any producer runs.
+ */
+int lowm_push_wait(const uint32_t* flags, int n_flags, uint32_t flag_value,
+                   uint32_t timeout_us, int* missing, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

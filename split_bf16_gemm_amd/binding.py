@@ -111,6 +111,11 @@ class Library:
         lib.lowm_check_launch.restype = _i
         lib.lowm_pick_split_k.argtypes = [_i, _i, _i, ctypes.POINTER(_i)]
         lib.lowm_pick_split_k.restype = _i
+        lib.lowm_gemm_splitk_push.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _vp,
+                                              ctypes.c_uint32, _vp, ctypes.POINTER(Tactic)]
+        lib.lowm_gemm_splitk_push.restype = _i
+        lib.lowm_push_wait.argtypes = [_vp, _i, ctypes.c_uint32, ctypes.c_uint32, _vp, _vp]
+        lib.lowm_push_wait.restype = _i
         lib.lowm_gemm_splitk_batched.argtypes = [ctypes.POINTER(GemmDesc), _i, _i, _i, _i, _vp,
                                                  _vp]
         lib.lowm_gemm_splitk_batched.restype = _i
@@ -170,6 +175,18 @@ class Library:
              out_dtype: torch.dtype = torch.bfloat16, tactic: Optional[Tactic] = None,
              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
         """C = A @ W.T on the GPU (A [M,K], W [N,K] bf16) through the C ABI."""
+        M, N, K = self._operands(A, W)
+        f32out = out_dtype == torch.float32
+        out = self._out(out, M, N, out_dtype, A.device)
+        ws_ptr = self._workspace_ptr(workspace, M, N, K, split_k)
+        s = stream if stream is not None else torch.cuda.current_stream(A.device)
+        rc = self.call_raw(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, split_k,
+                           ws_ptr, s.cuda_stream, f32out, tactic)
+        self.check(rc)
+        return out
+
+    @staticmethod
+    def _operands(A, W):
         if A.dim() != 2 or W.dim() != 2 or A.shape[1] != W.shape[1]:
             raise ValueError(f"shapes {tuple(A.shape)} and {tuple(W.shape)} do not chain")
         if A.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
@@ -178,27 +195,58 @@ class Library:
             raise ValueError("A and W must be on the GPU")
         if not (A.is_contiguous() and W.is_contiguous()):
             raise ValueError("A and W must be contiguous row-major")
-        M, K = A.shape
-        N = W.shape[0]
-        f32out = out_dtype == torch.float32
+        return A.shape[0], W.shape[0], A.shape[1]
+
+    @staticmethod
+    def _out(out, M, N, dtype, device):
         if out is None:
-            out = torch.empty((M, N), dtype=out_dtype, device=A.device)
-        if out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous():
+            out = torch.empty((M, N), dtype=dtype, device=device)
+        if out.shape != (M, N) or out.dtype != dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous [M, N] tensor of out_dtype")
-        ws_ptr = 0
-        if split_k > 1:
-            need = self.workspace_bytes(M, N, K, split_k)
-            if workspace is None:
-                raise ValueError(f"split_k={split_k} needs a zeroed workspace of {need} bytes "
-                                 "(make_workspace)")
-            if workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
-                raise ValueError(f"workspace smaller than {need} bytes")
-            ws_ptr = workspace.data_ptr()
-        s = stream if stream is not None else torch.cuda.current_stream(A.device)
-        rc = self.call_raw(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, split_k,
-                           ws_ptr, s.cuda_stream, f32out, tactic)
-        self.check(rc)
         return out
+
+    def _workspace_ptr(self, workspace, M, N, K, split_k) -> int:
+        if split_k <= 1:
+            return 0
+        need = self.workspace_bytes(M, N, K, split_k)
+        if workspace is None:
+            raise ValueError(f"split_k={split_k} needs a zeroed workspace of {need} bytes "
+                             "(make_workspace)")
+        if workspace.numel() * workspace.element_size() < need or not workspace.is_cuda:
+            raise ValueError(f"workspace smaller than {need} bytes")
+        return workspace.data_ptr()
+
+    def gemm_push(self, A, W, split_k, push, flags, flag_value, out=None, workspace=None,
+                  tactic=None, stream=None):
+        """C = A @ W.T with the push epilogue: every output tile also goes to
+        `push` (a bf16 [M, >= N] view whose rows may be strided, last dim
+        contiguous) and then flag j (columns 16j..16j+15) of `flags` (int32
+        or uint32 bits) is set to flag_value."""
+        M, N, K = self._operands(A, W)
+        out = self._out(out, M, N, torch.bfloat16, A.device)
+        if push.dtype != torch.bfloat16 or push.dim() != 2 or push.shape[0] != M or \
+                push.shape[1] < N or push.stride(1) != 1 or not push.is_cuda:
+            raise ValueError("push must be a bf16 GPU view of shape [M, >= N], unit column stride")
+        if flags.dtype != torch.int32 or flags.numel() < (N + 15) // 16 or not flags.is_cuda \
+                or not flags.is_contiguous():
+            raise ValueError(f"flags must be a contiguous int32 GPU tensor of >= {(N + 15) // 16}")
+        ws_ptr = self._workspace_ptr(workspace, M, N, K, split_k)
+        s = stream if stream is not None else torch.cuda.current_stream(A.device)
+        tp = ctypes.byref(tactic) if tactic is not None else None
+        self.check(self.lib.lowm_gemm_splitk_push(
+            A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, split_k, ws_ptr,
+            push.data_ptr(), push.stride(0), flags.data_ptr(), flag_value, s.cuda_stream, tp))
+        return out
+
+    def push_wait(self, flags, n_flags: int, flag_value: int, timeout_us: int, missing,
+                  stream=None):
+        """Enqueue the bounded wait for flags[0:n_flags] == flag_value; the count
+        of flags not seen set lands in missing[0] (an int32 GPU tensor)."""
+        if missing.dtype != torch.int32 or not missing.is_cuda or flags.dtype != torch.int32:
+            raise ValueError("flags and missing must be int32 GPU tensors")
+        s = stream if stream is not None else torch.cuda.current_stream(flags.device)
+        self.check(self.lib.lowm_push_wait(flags.data_ptr(), n_flags, flag_value, timeout_us,
+                                           missing.data_ptr(), s.cuda_stream))
 
     @staticmethod
     def descs(As, Ws, Cs):

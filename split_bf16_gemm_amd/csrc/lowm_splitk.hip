@@ -106,6 +106,8 @@ enum TraceSlot : int {
 };
 
 struct Args {
+  // Every field a single-GEMM launch reads sits in the first 64 bytes of the
+  // argument segment, so each workgroup's start waits for one scalar line.
   const uint16_t* A;
   const uint16_t* W;
   void* C;
@@ -113,10 +115,17 @@ struct Args {
   float* part;            // [tiles][S][M*BN] fp32 partials
   int M, N, K, S;
   int nvec;               // 16-byte vectors per rank slice: K / S / 8
-  int tiles;              // ceil(N / BN)
+  int batch;              // GEMMs in the launch; 1: these fields describe the only one
+  // Set by gemm_args in the kernel, never read from the argument segment.
   int bid_base;           // first workgroup of this GEMM in a batched launch
+  // push epilogue (its own instantiation, bf16 output)
+  uint16_t* push;         // exchange buffer, element (m, n) at push[m * push_ld + n]
+  uint32_t* flags;        // [ceil(N / 16)] one per 16 output columns
+  int push_ld;
+  uint32_t flag_value;
   StressArgs stress;
 };
+static_assert(offsetof(Args, batch) + sizeof(int) <= 64, "hot fields leave the first line");
 
 // Batched launch: up to kMaxBatch independent GEMMs with one M, K and split_k
 // in one grid.  GEMM g owns the workgroups [bid_end of g-1, bid_end of g),
@@ -129,22 +138,21 @@ struct GemmSlot {
   uint32_t* ctr;
   float* part;
   int N;
-  int tiles;
   int bid_end;
 };
 struct Batch {
-  int count;              // 1: Args describes the only GEMM
-  GemmSlot g[kMaxBatch];
+  GemmSlot g[kMaxBatch];  // read only when Args::batch > 1
 };
 
 // The Args of the GEMM this workgroup belongs to.
 __device__ __forceinline__ Args gemm_args(const Args& a, const Batch& bt) {
   Args b = a;
-  if (bt.count > 1) {
+  b.bid_base = 0;
+  if (a.batch > 1) {
     int g = 0;
 #pragma unroll
     for (int i = 0; i < kMaxBatch - 1; ++i)
-      if (i < bt.count - 1 && (int)blockIdx.x >= bt.g[i].bid_end) g = i + 1;
+      if (i < a.batch - 1 && (int)blockIdx.x >= bt.g[i].bid_end) g = i + 1;
     const GemmSlot& s = bt.g[g];
     b.A = s.A;
     b.W = s.W;
@@ -152,7 +160,6 @@ __device__ __forceinline__ Args gemm_args(const Args& a, const Batch& bt) {
     b.ctr = s.ctr;
     b.part = s.part;
     b.N = s.N;
-    b.tiles = s.tiles;
     b.bid_base = g > 0 ? bt.g[g - 1].bid_end : 0;
   }
   return b;
@@ -274,8 +281,17 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Output kinds a kernel is instantiated for: bf16, fp32, and bf16 with the
+// push epilogue (a separate instantiation, so the plain kernels carry no
+// trace of it).
+struct PushBf16 {};
+template <typename OutT> struct OutStore { using type = OutT; };
+template <> struct OutStore<PushBf16> { using type = __bf16; };
 template <typename OutT>
-__device__ __forceinline__ OutT to_out(float v);
+constexpr bool kPush = std::is_same<OutT, PushBf16>::value;
+
+template <typename T>
+__device__ __forceinline__ T to_out(float v);
 template <>
 __device__ __forceinline__ float to_out<float>(float v) { return v; }
 template <>
@@ -362,6 +378,34 @@ __device__ __forceinline__ void wait_groups(int younger) {
   else wait_vmcnt<3 * N <= 63 ? 3 * N : 63>();
 }
 
+// a6: the owner's store of output element (m, n), to C and, with the push
+// epilogue, to the exchange buffer.  The pushed copy is written with
+// system-scope stores (sc0 sc1: through every cache to memory), so once they
+// are acknowledged a flag store publishes them to any observer.
+template <typename OutT>
+__device__ __forceinline__ void store_out(const Args& a, int m, int n, float v) {
+  using T = typename OutStore<OutT>::type;
+  const T o = to_out<T>(v);
+  static_cast<T*>(a.C)[(size_t)m * a.N + n] = o;
+  if constexpr (kPush<OutT>)
+    __hip_atomic_store(a.push + (size_t)m * a.push_ld + n, __builtin_bit_cast(uint16_t, o),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Push epilogue, called by the one wavefront that stored the tile at
+// columns n0 .. n0+16*RG-1: once every pushed store of it is acknowledged,
+// set the flag of each of its 16-column groups to the caller's value.
+template <int RG, typename OutT>
+__device__ __forceinline__ void publish_flags(const Args& a, int n0, int lane) {
+  if constexpr (kPush<OutT>) {
+    wait_vmcnt0();
+    pin_issue();
+    if (lane < RG && n0 + 16 * lane < a.N)
+      __hip_atomic_store(a.flags + n0 / 16 + lane, a.flag_value, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The epilogue of a workgroup of kWaves wavefronts, each holding its own sums
 // of the tile (acc, MFMA D layout).  The sums are added through LDS in
@@ -406,13 +450,12 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
     for (int w = 1; w < kWaves; ++w) p += red_at(w, rg, b, i, ln);
     return p;
   };
-  OutT* C = static_cast<OutT*>(a.C);
-
   if (a.S == 1) {
     for (int e = lane; e < E; e += kWave) {
       const int m = e / BN, n = n0 + (e - m * BN);
-      if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(rank_sum(e));
+      if (n < a.N) store_out<OutT>(a, m, n, rank_sum(e));
     }
+    publish_flags<RG, OutT>(a, n0, lane);
     LOWM_TRACE(kTraceEnd);
     return;
   }
@@ -449,8 +492,9 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   for (int e = lane; e < E; e += kWave) {
     const float v = fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
     const int m = e / BN, n = n0 + (e - m * BN);
-    if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);  // a6
+    if (n < a.N) store_out<OutT>(a, m, n, v);  // a6
   }
+  publish_flags<RG, OutT>(a, n0, lane);
   // The tile's counter is zero again for the next launch.
   if (lane == 0)
     __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
@@ -493,7 +537,7 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
   const int tile = (q / a.S) * kXcds + (bid % kXcds);
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
-  if (tile >= a.tiles) return;
+  if (tile * BN >= a.N) return;
   const int n0 = tile * BN;
   const int Ks = a.nvec * kVecK;
   const size_t k0 = (size_t)rank * Ks;
@@ -813,7 +857,7 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
   const int tile = (q / a.S) * kXcds + (bid % kXcds);
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
-  if (tile >= a.tiles) return;
+  if (tile * BN >= a.N) return;
   const int n0 = tile * BN;
   const int nvec = a.nvec;
   // line pairs (64 K each) per wavefront; the launch requires nvec % 32 == 0
@@ -1030,7 +1074,7 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   const int tile = (q / a.S) * kXcds + (bid % kXcds);
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
-  if (tile >= a.tiles) return;
+  if (tile * BN >= a.N) return;
   const int n0 = tile * BN;
   const int nvec = a.nvec;
   const size_t k0 = (size_t)rank * nvec * kVecK;
@@ -1163,7 +1207,6 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
 #pragma unroll
     for (int b = 0; b < MB; ++b) sum[rg][b] = acc[0][rg][b] + acc[1][rg][b];
 
-  OutT* C = static_cast<OutT*>(a.C);
   if (a.S == 1) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
@@ -1172,8 +1215,9 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = 16 * b + 4 * g + i, n = n0 + 16 * rg + l16;
-          if (m < a.M && n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(sum[rg][b][i]);
+          if (m < a.M && n < a.N) store_out<OutT>(a, m, n, sum[rg][b][i]);
         }
+    publish_flags<RG, OutT>(a, n0, lane);
     LOWM_TRACE(kTraceEnd);
     return;
   }
@@ -1217,8 +1261,9 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
         const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16, n = n0 + nl;
         if (m >= a.M) continue;
         const float v = fold_ranks(slots, E, m * BN + nl, a.S, rank, sum[rg][b][i]);
-        if (n < a.N) C[(size_t)m * a.N + n] = to_out<OutT>(v);
+        if (n < a.N) store_out<OutT>(a, m, n, v);
       }
+  publish_flags<RG, OutT>(a, n0, lane);
   if (lane == 0)
     __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -1292,9 +1337,10 @@ constexpr int rg_index(int rg) {
   return -1;
 }
 
-// table[out][act][MB-1][rg_index][variant]
+// table[out][act][MB-1][rg_index][variant]; out 0 bf16, 1 fp32, 2 bf16 + push
+enum OutKind : int { kOutBf16 = 0, kOutF32 = 1, kOutPush = 2, kNumOutKinds = 3 };
 struct Table {
-  KernelFn fn[2][2][4][kNumRowGroups][kNumVariants];
+  KernelFn fn[kNumOutKinds][2][4][kNumRowGroups][kNumVariants];
 };
 template <typename OutT, int MB, int RG>
 void fill_one(Table& t, int out) {
@@ -1318,8 +1364,9 @@ void fill_out(Table& t, int out) {
 const Table& table() {
   static const Table t = [] {
     Table x{};
-    fill_out<__bf16>(x, 0);
-    fill_out<float>(x, 1);
+    fill_out<__bf16>(x, kOutBf16);
+    fill_out<float>(x, kOutF32);
+    fill_out<PushBf16>(x, kOutPush);
     return x;
   }();
   return t;
@@ -1353,12 +1400,12 @@ int rows_index(int rows) { return rows % 16 == 0 ? rg_index(rows / 16) : -1; }
 
 int threads_of(const lowm_tactic& t) { return t.stage == kStageWave ? kWave : kThreads; }
 
-KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t) {
+KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t, bool push = false) {
   if (t.waves != (t.stage == kStageWave ? 1 : kWaves)) return nullptr;
   const int ri = rows_index(t.rows);
   const int vi = variant_index(t);
   if (ri < 0 || vi < 0 || M < 1 || M > LOWM_MAX_M) return nullptr;
-  return table().fn[f32out ? 1 : 0][act][(M + 15) / 16 - 1][ri][vi];
+  return table().fn[push ? kOutPush : f32out ? kOutF32 : kOutBf16][act][(M + 15) / 16 - 1][ri][vi];
 }
 
 // Largest activation slice staged in LDS (bytes, padding included).
@@ -1470,18 +1517,19 @@ int pick_split(int M, int N, int K, int* split_k) {
 // The kernel a launch with tactic t runs: the activation slice is staged in
 // LDS when it is small and whole 1 KB pieces (and the build has that
 // instantiation); otherwise the wavefronts load activation operands from L2.
-KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_t* dyn_lds) {
+KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_t* dyn_lds,
+                       bool push = false) {
   *dyn_lds = 0;
   // line-pair tiles stream whole 64-K line pairs per wavefront
   if (t.stage == kStageLine && nvec % 32 != 0) return nullptr;
   if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
-    if (KernelFn fn = lookup(f32out, 1, M, t)) {
+    if (KernelFn fn = lookup(f32out, 1, M, t, push)) {
       *dyn_lds = act_lds_bytes(M, nvec);
       return fn;
     }
   }
   *dyn_lds = 0;
-  return lookup(f32out, 0, M, t);
+  return lookup(f32out, 0, M, t, push);
 }
 
 size_t workspace_bytes(int M, int N, int K, int S) {
@@ -1492,13 +1540,47 @@ size_t workspace_bytes(int M, int N, int K, int S) {
   return counter_bytes(N) + (size_t)S * (size_t)M * round_up((size_t)N, kPartialPad) * sizeof(float);
 }
 
+// The push epilogue of a single-GEMM launch (bf16 output).
+struct PushSpec {
+  void* dst;
+  int ld;
+  uint32_t* flags;
+  uint32_t value;
+};
+
+// [lo, hi) of the bytes a row-major [rows, cols] array with row pitch ld
+// elements of `elem` bytes spans.
+inline void byte_span(const void* p, int rows, int cols, int ld, size_t elem, uintptr_t* lo,
+                      uintptr_t* hi) {
+  *lo = (uintptr_t)p;
+  *hi = *lo + ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * elem;
+}
+
+int check_push(const PushSpec& p, const void* C, int M, int N) {
+  if (!p.dst || !p.flags || p.value == 0 || p.ld < N) return LOWM_ERR_INVALID_ARG;
+  if (((uintptr_t)p.dst & 1) || ((uintptr_t)p.flags & 3)) return LOWM_ERR_UNSUPPORTED;
+  uintptr_t c0, c1, d0, d1, f0, f1;
+  byte_span(C, M, N, N, 2, &c0, &c1);
+  byte_span(p.dst, M, N, p.ld, 2, &d0, &d1);
+  byte_span(p.flags, 1, (N + 15) / 16, 0, 4, &f0, &f1);
+  auto overlap = [](uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+    return a0 < b1 && b0 < a1;
+  };
+  if (overlap(c0, c1, d0, d1) || overlap(c0, c1, f0, f1) || overlap(d0, d1, f0, f1))
+    return LOWM_ERR_INVALID_ARG;
+  return LOWM_OK;
+}
+
 // One launch of `count` GEMMs sharing M, K, split_k, the output type and the
 // tactic; the single-GEMM entry points are the count == 1 case.  GEMM g's
 // workspace follows GEMM g-1's (each is workspace_bytes of its own sizes).
+// `push` (single bf16 GEMM only) adds the push epilogue.
 int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int K, int S,
-                 void* workspace, hipStream_t stream, const lowm_tactic* tactic) {
+                 void* workspace, hipStream_t stream, const lowm_tactic* tactic,
+                 const PushSpec* push = nullptr) {
   if (!gemms || count < 1) return LOWM_ERR_INVALID_ARG;
   if (count > kMaxBatch) return LOWM_ERR_UNSUPPORTED;
+  if (push && (count != 1 || f32out)) return LOWM_ERR_INVALID_ARG;
   for (int g = 0; g < count; ++g)
     if (!gemms[g].A || !gemms[g].W || !gemms[g].C) return LOWM_ERR_INVALID_ARG;
   int rc = LOWM_OK;
@@ -1512,6 +1594,10 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     if ((uintptr_t)gemms[g].C & (f32out ? 3 : 1)) return LOWM_ERR_UNSUPPORTED;
   }
   if (S > 1 && ((uintptr_t)workspace & 15)) return LOWM_ERR_UNSUPPORTED;
+  if (push) {
+    rc = check_push(*push, gemms[0].C, M, gemms[0].N);
+    if (rc != LOWM_OK) return rc;
+  }
 
   lowm_tactic t;
   if (tactic) {
@@ -1522,12 +1608,11 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
   }
   const int nvec = K / S / kVecK;
   size_t dyn_lds = 0;
-  const KernelFn fn = select_kernel(f32out, M, nvec, t, &dyn_lds);
+  const KernelFn fn = select_kernel(f32out, M, nvec, t, &dyn_lds, push != nullptr);
   if (!fn) return LOWM_ERR_UNSUPPORTED;
 
   const int BN = t.rows;
-  Batch bt;
-  bt.count = count;
+  Batch bt{};
   size_t grid = 0, ws_off = 0;
   for (int g = 0; g < count; ++g) {
     GemmSlot& sl = bt.g[g];
@@ -1536,18 +1621,18 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     sl.W = static_cast<const uint16_t*>(gemms[g].W);
     sl.C = gemms[g].C;
     sl.N = N;
-    sl.tiles = (N + BN - 1) / BN;
     char* ws = static_cast<char*>(workspace) + ws_off;
     sl.ctr = S > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
     sl.part = S > 1 ? reinterpret_cast<float*>(ws + counter_bytes(N)) : nullptr;
     ws_off += workspace_bytes(M, N, K, S);
-    grid += round_up((size_t)sl.tiles, kXcds) * (size_t)S;
+    const size_t tiles = (size_t)((N + BN - 1) / BN);
+    grid += round_up(tiles, kXcds) * (size_t)S;
     if (grid > 0x7fffffffu) return LOWM_ERR_UNSUPPORTED;
     sl.bid_end = (int)grid;
   }
   for (int g = count; g < kMaxBatch; ++g) bt.g[g] = bt.g[count - 1];
 
-  Args a;
+  Args a{};
   a.A = bt.g[0].A;
   a.W = bt.g[0].W;
   a.C = bt.g[0].C;
@@ -1556,10 +1641,14 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
   a.K = K;
   a.S = S;
   a.nvec = nvec;
-  a.tiles = bt.g[0].tiles;
+  a.batch = count;
   a.ctr = bt.g[0].ctr;
   a.part = bt.g[0].part;
   a.bid_base = 0;
+  a.push = push ? static_cast<uint16_t*>(push->dst) : nullptr;
+  a.flags = push ? push->flags : nullptr;
+  a.push_ld = push ? push->ld : 0;
+  a.flag_value = push ? push->value : 0u;
   a.stress = g_stress;
 
   void* kargs[] = {&a, &bt};
@@ -1574,9 +1663,62 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
 }
 
 int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int K, int S,
-           void* workspace, hipStream_t stream, const lowm_tactic* tactic) {
+           void* workspace, hipStream_t stream, const lowm_tactic* tactic,
+           const PushSpec* push = nullptr) {
   const lowm_gemm_desc one = {A, W, C, N};
-  return launch_batch(&one, 1, f32out, M, K, S, workspace, stream, tactic);
+  return launch_batch(&one, 1, f32out, M, K, S, workspace, stream, tactic, push);
+}
+
+// Consumer side of the push epilogue: one wavefront polls the flags with
+// system-scope loads until each holds `value` or `ticks` of the 100 MHz
+// real-time counter have passed, then writes how many flags it did not see
+// set (0: all were).  Every poll of a flag is a fresh load; a flag once seen
+// is not polled again.
+constexpr int kWaitFlagsPerLane = 64;
+constexpr int kMaxWaitFlags = kWave * kWaitFlagsPerLane;
+constexpr uint32_t kMaxWaitUs = 10u * 1000u * 1000u;
+
+__global__ __launch_bounds__(kWave) void lowm_push_wait_kernel(const uint32_t* flags, int n,
+                                                                uint32_t value, uint64_t ticks,
+                                                                int* missing) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x;
+  uint64_t pending = 0;   // bit j: flag lane + 64 j not yet seen
+  for (int j = 0; j < kWaitFlagsPerLane; ++j)
+    if (lane + kWave * j < n) pending |= 1ull << j;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    for (int j = 0; j < kWaitFlagsPerLane; ++j) {
+      if (!(pending >> j & 1)) continue;
+      const uint32_t f = __hip_atomic_load(flags + lane + kWave * j, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+      if (f == value) pending &= ~(1ull << j);
+    }
+    if (__all(pending == 0)) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  int left = __popcll(pending);
+  for (int off = kWave / 2; off > 0; off >>= 1) left += __shfl_xor(left, off);
+  if (lane == 0) missing[0] = left;
+#endif
+}
+
+int push_wait(const uint32_t* flags, int n, uint32_t value, uint32_t timeout_us, int* missing,
+              hipStream_t stream) {
+  if (!flags || !missing || n < 1 || value == 0) return LOWM_ERR_INVALID_ARG;
+  if (n > kMaxWaitFlags || timeout_us > kMaxWaitUs) return LOWM_ERR_UNSUPPORTED;
+  if (((uintptr_t)flags & 3) || ((uintptr_t)missing & 3)) return LOWM_ERR_UNSUPPORTED;
+  const uint64_t ticks = (uint64_t)timeout_us * 100u;
+  void* kargs[] = {&flags, &n, &value, const_cast<uint64_t*>(&ticks), &missing};
+  hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&lowm_push_wait_kernel),
+                                   dim3(1), dim3(kWave), kargs, 0, stream);
+  if (err == hipSuccess) err = hipGetLastError();
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return LOWM_ERR_LAUNCH;
+  }
+  return LOWM_OK;
 }
 
 }  // namespace lowm
@@ -1613,6 +1755,21 @@ int lowm_gemm_splitk_f32out_ex(const void* A, const void* W, float* C, int M, in
 
 size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k) {
   return lowm::workspace_bytes(M, N, K, split_k);
+}
+
+int lowm_gemm_splitk_push(const void* A, const void* W, void* C, int M, int N, int K,
+                          int split_k, void* workspace, void* push, int push_ld,
+                          uint32_t* flags, uint32_t flag_value, void* stream,
+                          const lowm_tactic* tactic) {
+  const lowm::PushSpec ps = {push, push_ld, flags, flag_value};
+  return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
+                      static_cast<hipStream_t>(stream), tactic, &ps);
+}
+
+int lowm_push_wait(const uint32_t* flags, int n_flags, uint32_t flag_value,
+                   uint32_t timeout_us, int* missing, void* stream) {
+  return lowm::push_wait(flags, n_flags, flag_value, timeout_us, missing,
+                         static_cast<hipStream_t>(stream));
 }
 
 int lowm_gemm_splitk_batched(const lowm_gemm_desc* gemms, int count, int M, int K,

@@ -258,3 +258,46 @@ def test_check_launch_reports_validation_errors(lib):
     assert lib.check_launch(4, 64, 256, 2, tactic=binding.tactic("reg", 80, 4, 3)) == \
         binding.LOWM_ERR_UNSUPPORTED
     assert lib.check_launch(4, 64, 256, 2) == 0
+
+
+C_ADDR, PUSH_ADDR, FLAG_ADDR = 0x10000, 0x100000, 0x200000
+
+
+def push_call(lib, push=PUSH_ADDR, ld=64, flags=FLAG_ADDR, value=1, C=C_ADDR, M=4, N=64,
+              K=256, S=2, ws=FAKE):
+    return lib.lib.lowm_gemm_splitk_push(FAKE, FAKE, C, M, N, K, S, ws, push, ld, flags, value,
+                                         None, None)
+
+
+def test_push_validation(lib):
+    """Every case is rejected on the host, before any HIP call."""
+    E = binding
+    assert push_call(lib, push=0) == E.LOWM_ERR_INVALID_ARG
+    assert push_call(lib, flags=0) == E.LOWM_ERR_INVALID_ARG
+    assert push_call(lib, value=0) == E.LOWM_ERR_INVALID_ARG
+    assert push_call(lib, ld=63) == E.LOWM_ERR_INVALID_ARG
+    assert push_call(lib, push=PUSH_ADDR + 1) == E.LOWM_ERR_UNSUPPORTED
+    assert push_call(lib, flags=FLAG_ADDR + 2) == E.LOWM_ERR_UNSUPPORTED
+    # overlaps: C [0x10000, +4*64*2), push rows at ld 64
+    assert push_call(lib, push=C_ADDR + 256) == E.LOWM_ERR_INVALID_ARG
+    assert push_call(lib, flags=C_ADDR + 100) == E.LOWM_ERR_INVALID_ARG
+    assert push_call(lib, flags=PUSH_ADDR + 3 * 64 * 2) == E.LOWM_ERR_INVALID_ARG
+    # a wide push row pitch puts row 3 past the flags
+    assert push_call(lib, ld=(FLAG_ADDR - PUSH_ADDR) // 2) == E.LOWM_ERR_INVALID_ARG
+    # the GEMM's own checks still apply
+    assert push_call(lib, M=65) == E.LOWM_ERR_UNSUPPORTED
+    assert push_call(lib, ws=0) == E.LOWM_ERR_WORKSPACE
+    assert lib.lib.lowm_last_hip_error() == 0
+
+
+def test_push_wait_validation(lib):
+    w = lib.lib.lowm_push_wait
+    E = binding
+    assert w(FLAG_ADDR, 0, 1, 10, FAKE, None) == E.LOWM_ERR_INVALID_ARG
+    assert w(FLAG_ADDR, 4, 0, 10, FAKE, None) == E.LOWM_ERR_INVALID_ARG
+    assert w(0, 4, 1, 10, FAKE, None) == E.LOWM_ERR_INVALID_ARG
+    assert w(FLAG_ADDR, 4, 1, 10, 0, None) == E.LOWM_ERR_INVALID_ARG
+    assert w(FLAG_ADDR, 4097, 1, 10, FAKE, None) == E.LOWM_ERR_UNSUPPORTED
+    assert w(FLAG_ADDR, 4, 1, 10_000_001, FAKE, None) == E.LOWM_ERR_UNSUPPORTED
+    assert w(FLAG_ADDR + 2, 4, 1, 10, FAKE, None) == E.LOWM_ERR_UNSUPPORTED
+    assert lib.lib.lowm_last_hip_error() == 0

@@ -1,0 +1,137 @@
+"""Push epilogue: each output tile's owner also writes the bf16 tile into a
+caller-given exchange buffer and then sets one flag per 16 output columns.
+
+Checked here: the pushed copy is bit-identical to C (which is itself the
+plain launch's output), it lands exactly in the [M, N] window of a wider
+strided buffer and nowhere else, each flag of the GEMM holds the caller's
+value and the flags after them are untouched; a consumer that waits for the
+flags on a second stream while the GEMM runs sees every flag and the final
+values; the wait gives up, bounded, on flags that no launch sets."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import split_bf16_gemm_amd as sbg
+import workloads
+from gpu_util import device, inputs, say, to_bits
+from split_bf16_gemm_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -1          # 0xFFFF in every bf16 slot, all bits in every flag slot
+
+CASES = [  # M, N, K, split_k
+    (4, 6144, 4096, 2),
+    (4, 300, 2048, 1),
+    (4, 300, 2048, 4),
+    (20, 520, 2048, 2),
+    (1, 2304, 12288, 4),
+]
+
+TACTICS = [None, ("reg", 16, 4, 2), ("wave", 16, 4, 4), ("lds", 16, 4, 2), ("reg", 32, 4, 2)]
+
+
+def window(M, N, dev, off=24, extra=40):
+    ld = off + N + extra
+    big = torch.full((M, ld), SENTINEL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    return big, big[:, off:off + N], off
+
+
+@pytest.mark.parametrize("M,N,K,S", CASES)
+@pytest.mark.parametrize("tac", TACTICS, ids=lambda t: "default" if t is None else ":".join(map(str, t)))
+def test_push_copy_window_and_flags(M, N, K, S, tac):
+    lib = sbg.load()
+    dev = device()
+    wl = workloads.Workload(f"push_m{M}_n{N}_k{K}_s{S}", M, N, K, S, seed_a=31, seed_w=32)
+    A, W = (t.to(dev) for t in inputs(wl))
+    tactic = None if tac is None else binding.tactic(*tac)
+    nflags = (N + 15) // 16
+    flags = torch.full((nflags + 8,), SENTINEL, dtype=torch.int32, device=dev)
+    flags[:nflags] = 0
+    big, win, off = window(M, N, dev)
+    ws = lib.make_workspace(M, N, K, S, dev)
+    say("push", M, N, K, S, tac)
+    try:
+        C = lib.gemm_push(A, W, S, win, flags, 7, workspace=ws, tactic=tactic)
+    except sbg.LowmError as e:
+        if tactic is not None and e.code == binding.LOWM_ERR_UNSUPPORTED:
+            pytest.skip(f"tactic {tac} is not built for M {M}")
+        raise
+    torch.cuda.synchronize()
+    plain = lib.gemm(A, W, S, workspace=ws, tactic=tactic)
+    torch.cuda.synchronize()
+    c = to_bits(C)
+    assert np.array_equal(c, to_bits(plain)), "C of the push launch differs from the plain launch"
+    b = to_bits(big)
+    assert np.array_equal(b[:, off:off + N], c), "pushed copy differs from C"
+    outside = np.ones(b.shape, dtype=bool)
+    outside[:, off:off + N] = False
+    assert (b[outside] == 0xFFFF).all(), "the push wrote outside its [M, N] window"
+    f = flags.cpu().numpy()
+    assert (f[:nflags] == 7).all(), "a flag of the GEMM was not set"
+    assert (f[nflags:] == SENTINEL).all(), "a flag past the GEMM's columns was written"
+    if ws is not None:
+        assert not ws[:sbg.counter_bytes(N)].cpu().numpy().any()
+
+
+def test_push_consumer_waits_on_another_stream():
+    """The wait is enqueued first on a second stream; it must see every flag
+    raised by the GEMM that runs after it on the current stream, and the data
+    it copies afterwards must be the final output."""
+    lib = sbg.load()
+    dev = device()
+    M, N, K, S = 4, 6144, 4096, 2
+    wl = workloads.Workload("push_consumer", M, N, K, S, seed_a=41, seed_w=42)
+    A, W = (t.to(dev) for t in inputs(wl))
+    nflags = (N + 15) // 16
+    flags = torch.zeros(nflags, dtype=torch.int32, device=dev)
+    missing = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    big, win, _ = window(M, N, dev)
+    got = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = lib.make_workspace(M, N, K, S, dev)
+    consumer = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    say("push consumer wait + producer")
+    lib.push_wait(flags, nflags, 3, 2_000_000, missing, stream=consumer)
+    with torch.cuda.stream(consumer):
+        got.copy_(win)
+    C = lib.gemm_push(A, W, S, win, flags, 3, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(missing.item()) == 0, f"the consumer timed out with {int(missing.item())} flags unseen"
+    assert np.array_equal(to_bits(got), to_bits(C)), "the consumer read values before the final ones"
+
+
+def test_push_wait_times_out_on_flags_never_set():
+    lib = sbg.load()
+    dev = device()
+    flags = torch.zeros(100, dtype=torch.int32, device=dev)
+    flags[::3] = 5
+    missing = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    say("push wait timeout")
+    lib.push_wait(flags, 100, 5, 2000, missing)
+    torch.cuda.synchronize()
+    assert int(missing.item()) == 100 - 34
+
+
+def test_push_flag_value_per_call():
+    """Two launches on the same flags with different values, no reset between."""
+    lib = sbg.load()
+    dev = device()
+    M, N, K, S = 4, 1000, 2048, 2
+    wl = workloads.Workload("push_twice", M, N, K, S, seed_a=51, seed_w=52)
+    A, W = (t.to(dev) for t in inputs(wl))
+    nflags = (N + 15) // 16
+    flags = torch.zeros(nflags, dtype=torch.int32, device=dev)
+    dst = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = lib.make_workspace(M, N, K, S, dev)
+    missing = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    say("push twice")
+    for value in (1, 2):
+        C = lib.gemm_push(A, W, S, dst, flags, value, workspace=ws)
+        lib.push_wait(flags, nflags, value, 1_000_000, missing)
+        torch.cuda.synchronize()
+        assert int(missing.item()) == 0
+        assert (flags.cpu().numpy() == value).all()
+        assert np.array_equal(to_bits(dst), to_bits(C))
