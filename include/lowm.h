@@ -12,8 +12,11 @@
  * ("rank") produces an fp32 partial of the output tile and one owner adds the
  * partials, always in rank order 0, 1, ..., split_k-1, then rounds once to
  * bf16 (round-to-nearest-even) and is the only writer of C.  The owner is the
- * last rank of the tile to arrive (a per-tile counter in the workspace), so no
- * workgroup ever waits for another and any grid size is deadlock-free.
+ * last rank of the tile to arrive (a per-tile counter in the workspace), or,
+ * for split_k 2..4 and M * 16 <= 64, the tile's last rank when it finds every
+ * peer's partial already in the workspace.  That rank polls for at most 20 us
+ * and then arrives like any other, so no workgroup waits for another without
+ * a bound and any grid size completes.
  *
  * Layouts: A, W and C are dense row-major with no padding: element (m, k) of A
  * at A + m*K + k, (n, k) of W at W + n*K + k, (m, n) of C at C + m*N + n.
@@ -29,13 +32,15 @@
  * Workspace (split_k > 1 only): an opaque device buffer of
  * lowm_gemm_splitk_workspace_bytes(M, N, K, split_k) bytes, 256-byte aligned,
  * holding one arrival counter per output tile, each on its own 256-byte line
- * (256 * ceil(N / 16) bytes), followed by the fp32 partials.
- * Zero it once before first use (hipMemset).  Every launch that completes
- * leaves all counters at zero again (the owner resets its tile's counter), so
- * the workspace can be reused by the next launch without clearing; the
- * partial region is scratch and may hold anything between launches.  One
- * workspace per in-flight launch: launches that overlap in time (two streams)
- * must not share one.  After a launch that did not complete, zero it again.
+ * (256 * ceil(N / 16) bytes), followed by the partial slots (one 32-bit word
+ * per rank and tile element: the complement of the fp32 partial's bits, so
+ * that zero means "not published").  Zero it once before first use
+ * (hipMemset).  Every launch that completes leaves the whole workspace zero
+ * again (the owner resets its tile's counter and every slot of the tile), so
+ * it can be reused by the next launch, of any shape, without clearing; a
+ * caller must not write to it between launches.  One workspace per in-flight
+ * launch: launches that overlap in time (two streams) must not share one.
+ * After a launch that did not complete, zero it again.
  *
  * Errors: every int-returning function returns LOWM_OK (0) or a negative
  * LOWM_ERR_* code; lowm_strerror() names it and lowm_last_hip_error() gives

@@ -65,6 +65,8 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kVecK = 8;         // bf16 per 16-byte vector
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kCtrStride = 64;   // uint32 words between tile counters (256 bytes)
+constexpr int kProbeRanks = 3;   // early probe: at most 3 peers (split_k <= 4)
+constexpr uint32_t kProbeTicks = 2000;  // ... polled for at most 20 us (100 MHz clock)
 
 enum Stage : int {
   kStageLds = LOWM_STAGE_LDS,
@@ -112,7 +114,7 @@ struct Args {
   const uint16_t* W;
   void* C;
   uint32_t* ctr;          // [tiles] arrival counters, kCtrStride words apart
-  float* part;            // [tiles][S][M*BN] fp32 partials
+  uint32_t* part;         // [tiles][S][M*BN] encoded fp32 partials
   int M, N, K, S;
   int nvec;               // 16-byte vectors per rank slice: K / S / 8
   int batch;              // GEMMs in the launch; 1: these fields describe the only one
@@ -136,7 +138,7 @@ struct GemmSlot {
   const uint16_t* W;
   void* C;
   uint32_t* ctr;
-  float* part;
+  uint32_t* part;
   int N;
   int bid_end;
 };
@@ -302,28 +304,51 @@ __device__ __forceinline__ __bf16 to_out<__bf16>(float v) {
 // ---------------------------------------------------------------------------
 // split-K fold helpers
 // ---------------------------------------------------------------------------
-// Device-scope (sc1) load of a peer's partial.
-__device__ __forceinline__ float load_partial(const float* p) {
+// Partial slots.  A slot word holds the complement of the bits of an fp32
+// partial, so the all-zero word means "not published".  The caller zero-fills
+// the workspace once; every tile's owner returns each slot it read, and its
+// own, to zero, so every launch starts with an all-zero partial region.  A
+// slot read before its rank wrote it therefore decodes as a NaN (~0), and a
+// late rank can tell from the slots alone whether a peer has published.  The
+// one fp32 pattern whose complement is zero (0xFFFFFFFF, a NaN) is stored as
+// the canonical NaN.
+__device__ __forceinline__ uint32_t enc_partial(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return ~(b == 0xFFFFFFFFu ? 0x7FC00000u : b);
+}
+__device__ __forceinline__ float dec_partial(uint32_t w) { return __builtin_bit_cast(float, ~w); }
+
+// Device-scope (sc1) accesses of the slots: written through the XCD's L2 to
+// where every XCD reads, and read from there.
+__device__ __forceinline__ uint32_t load_slot(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_slot(uint32_t* p, uint32_t w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The owner's value of one output element: the S rank partials of this tile
 // (slot r at slots[r * E + e]) added in rank order 0..S-1, with this rank's
-// own partial `own` at its own position.  The peers' loads are all issued
-// before the first add so they overlap instead of following one another.
+// own partial `own` at its own position.  The S-1 peers' slots are loaded
+// unconditionally (peer i is rank i, or i+1 past the owner) and before the
+// first add, so the loads overlap; a load under a branch would be waited for
+// inside it.  Loads only: the caller stores C and clears the slots after all
+// its folds, so that no wait for these loads also waits for stores.
 template <int SN>
-__device__ __forceinline__ float fold_ranks_n(const float* slots, size_t E, int e, int rank,
+__device__ __forceinline__ float fold_ranks_n(const uint32_t* slots, size_t E, int e, int rank,
                                               float own) {
-  float p[SN];
+  uint32_t w[SN - 1];
 #pragma unroll
-  for (int r = 0; r < SN; ++r) p[r] = (r == rank) ? own : load_partial(slots + (size_t)r * E + e);
-  float v = p[0];
+  for (int i = 0; i < SN - 1; ++i)
+    w[i] = load_slot(slots + (size_t)(i < rank ? i : i + 1) * E + e);
+  float v = (rank == 0) ? own : dec_partial(w[0]);
 #pragma unroll
-  for (int r = 1; r < SN; ++r) v += p[r];
+  for (int r = 1; r < SN; ++r)
+    v += (r == rank) ? own : dec_partial(r < rank ? w[r < SN - 1 ? r : 0] : w[r - 1]);
   return v;
 }
 
-__device__ __forceinline__ float fold_ranks(const float* slots, size_t E, int e, int S,
+__device__ __forceinline__ float fold_ranks(const uint32_t* slots, size_t E, int e, int S,
                                             int rank, float own) {
   switch (S) {
     case 2: return fold_ranks_n<2>(slots, E, e, rank, own);
@@ -332,9 +357,46 @@ __device__ __forceinline__ float fold_ranks(const float* slots, size_t E, int e,
     case 8: return fold_ranks_n<8>(slots, E, e, rank, own);
     default: break;
   }
-  float v = (rank == 0) ? own : load_partial(slots + e);
-  for (int r = 1; r < S; ++r) v += (r == rank) ? own : load_partial(slots + (size_t)r * E + e);
+  float v = 0.f;
+  for (int r = 0; r < S; ++r) {
+    const uint32_t w = load_slot(slots + (size_t)r * E + e);
+    const float p = (r == rank) ? own : dec_partial(w);
+    v = (r == 0) ? p : v + p;
+  }
   return v;
+}
+
+// Every rank's slot of element e back to zero, once the owner has read them
+// (the owner's own too: it published before it knew it was the owner).
+__device__ __forceinline__ void clear_slots(uint32_t* slots, size_t E, int e, int S) {
+  for (int r = 0; r < S; ++r) store_slot(slots + (size_t)r * E + e, 0u);
+}
+
+// Whether a split-K tile's last rank polls its peers' slots instead of
+// publishing (see workgroup_epilogue): split_k 2..4 and tiles of at most 64
+// elements (one per lane).
+__device__ __forceinline__ bool early_probe(const Args& a, int BN) {
+  return a.S > 1 && a.S - 1 <= kProbeRanks && a.M * BN <= kWave;
+}
+
+// a0: workgroup -> (output tile, rank).  Workgroups are dealt to the 8 XCDs
+// round-robin; every rank of a tile gets the same blockIdx % 8, hence one
+// XCD.  Where the early probe applies the order is rank-major: the GEMM's
+// first T8 workgroups are rank 0 of tiles 0..T8-1, the next T8 rank 1, and
+// so on (T8 = tiles rounded up to a multiple of 8), so a tile's later ranks
+// tend to end their streams after its earlier ones have published.
+// Elsewhere the ranks of a tile are dispatched 8 workgroups apart.
+__device__ __forceinline__ void decode_tile(const Args& a, int BN, int& tile, int& rank) {
+  const int bid = (int)blockIdx.x - a.bid_base;
+  if (early_probe(a, BN)) {
+    const int t8 = ((a.N + BN - 1) / BN + kXcds - 1) / kXcds * kXcds;
+    rank = bid / t8;
+    tile = bid - rank * t8;
+  } else {
+    const int q = bid / kXcds;
+    rank = q % a.S;
+    tile = (q / a.S) * kXcds + (bid % kXcds);
+  }
 }
 
 // Register/LDS budget of a tactic.  Kept in one place so the host picker and
@@ -428,6 +490,23 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red_at(wave, rg, b, i, lane) = acc[rg][b][i];
+
+  // Early probe (split_k 2..4, tiles of at most 64 elements): wavefront 0 of
+  // the last rank loads the peers' slots of its element now, so the loads
+  // overlap the wavefront reduction.  Lanes without an element count as
+  // published.
+  const int E = a.M * BN;
+  uint32_t* slots = a.part + (size_t)tile * a.S * E;
+  uint32_t probe[kProbeRanks];
+#pragma unroll
+  for (int i = 0; i < kProbeRanks; ++i) probe[i] = 1u;
+  const bool probing = early_probe(a, BN) && rank == a.S - 1;
+  if (wave == 0 && probing) {
+#pragma unroll
+    for (int i = 0; i < kProbeRanks; ++i)
+      if (i < a.S - 1 && lane < E) probe[i] = load_slot(slots + (size_t)i * E + lane);
+  }
+
   // Every wavefront's sums are in LDS after the barrier; wavefront 0 carries
   // on alone.  (A variant where the last wavefront to arrive at an LDS
   // counter carried on, with no barrier, measured slower.)
@@ -440,7 +519,11 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   // (m, nl) = (e / BN, e % BN).  The MFMA keeps D[row][col] in lane
   // col + 16*(row/4), register row % 4; rows are activation rows, columns
   // weight rows.
-  const int E = a.M * BN;
+  auto red_pos = [&](int e) -> float& {   // wavefront 0's sum of element e
+    const int m = e / BN, nl = e - (e / BN) * BN;
+    const int b = m >> 4, mm = m & 15;
+    return red_at(0, nl >> 4, b, mm & 3, (nl & 15) + 16 * (mm >> 2));
+  };
   auto rank_sum = [&](int e) {
     const int m = e / BN, nl = e - (e / BN) * BN;
     const int b = m >> 4, mm = m & 15;
@@ -460,22 +543,74 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
     return;
   }
 
+  uint32_t* ctr = a.ctr + (size_t)tile * kCtrStride;
+  LOWM_STALL(kSitePublish, 0);
+  if (probing) {
+    // The last rank (rank-major dispatch: issued after every peer of its
+    // tile on the same XCD) polls until every peer's slot holds its partial,
+    // for at most kProbeTicks; a peer's slot is visible without its
+    // publish acknowledgement and arrival, which the loaded memory system
+    // delays by microseconds.  Past the limit it publishes and arrives like
+    // any rank, so the result never depends on the dispatch order.
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      bool seen = true;
+#pragma unroll
+      for (int i = 0; i < kProbeRanks; ++i) seen = seen && probe[i] != 0u;
+      if (__all(seen)) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kProbeTicks) break;
+      __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+      for (int i = 0; i < kProbeRanks; ++i)
+        if (i < a.S - 1 && lane < E && probe[i] == 0u)
+          probe[i] = load_slot(slots + (size_t)i * E + lane);
+    }
+    bool seen = true;
+#pragma unroll
+    for (int i = 0; i < kProbeRanks; ++i) seen = seen && probe[i] != 0u;
+    if (__all(seen)) {
+      // Every peer has published: this rank is the owner without publishing
+      // or arriving.  No peer can become the owner, since only the S-1 peers
+      // arrive and the last of them sees S-2 earlier arrivals.  The fold is
+      // the same rank-order sum as the owner's below, this rank's partial
+      // last.  (Traced as a rank that never arrived.)
+      //
+      // Subtract the S-1 arrivals of the peers: whenever theirs land, the
+      // counter is back at zero for the next launch.  (Issued first: later,
+      // the compiler would wait for the stores below before it.)
+      if (lane == 0)
+        __hip_atomic_fetch_add(ctr, (uint32_t)(1 - a.S), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      LOWM_STALL(kSiteFold, 0);
+      if (lane < E) {
+        float v = dec_partial(probe[0]);
+#pragma unroll
+        for (int i = 1; i < kProbeRanks; ++i)
+          if (i < a.S - 1) v += dec_partial(probe[i]);
+        v += rank_sum(lane);
+        const int m = lane / BN, n = n0 + (lane - m * BN);
+        if (n < a.N) store_out<OutT>(a, m, n, v);  // a6
+#pragma unroll
+        for (int i = 0; i < kProbeRanks; ++i)
+          if (i < a.S - 1) store_slot(slots + (size_t)i * E + lane, 0u);
+      }
+      publish_flags<RG, OutT>(a, n0, lane);
+      LOWM_TRACE(kTraceEnd);
+      return;
+    }
+  }
+
   // a4: publish this rank's partial, then arrive.  The partial is written
   // with device-scope stores (sc1: written through this XCD's L2 to where
   // every XCD sees it) and the arrival is issued only after all of them are
   // acknowledged (vmcnt(0)): the release is carried by the stores' own
   // scope, so no cache-wide write-back is needed.
-  LOWM_STALL(kSitePublish, 0);
-  float* slots = a.part + (size_t)tile * a.S * E;
-  for (int e = lane; e < E; e += kWave)
-    __hip_atomic_store(slots + (size_t)rank * E + e, rank_sum(e), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  for (int e = lane; e < E; e += kWave) store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
   wait_vmcnt0();
   pin_issue();
   uint32_t before = 0;
   if (lane == 0)
-    before = __hip_atomic_fetch_add(a.ctr + (size_t)tile * kCtrStride, 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+    before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
   if (before != (uint32_t)(a.S - 1)) {   // not the last rank: done
@@ -487,18 +622,26 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   // (sc1), issued only after the arrival count is known, so they observe
   // every partial whose arrival was counted; no cache-wide invalidate.  The
   // fold is in rank order with this rank's partial, from LDS, at its own
-  // position.
+  // position; every slot read goes back to zero.
   LOWM_STALL(kSiteFold, 0);
+  // Two passes: the folds (global loads only, several elements' loads in
+  // flight at once; each result replaces the element's wavefront-0 sum in
+  // LDS, which nothing else reads), then the stores of C and the clearing
+  // of the slots, which nothing waits for.
+#pragma unroll 4
   for (int e = lane; e < E; e += kWave) {
     const float v = fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
+    red_pos(e) = v;
+  }
+  for (int e = lane; e < E; e += kWave) {
     const int m = e / BN, n = n0 + (e - m * BN);
-    if (n < a.N) store_out<OutT>(a, m, n, v);  // a6
+    if (n < a.N) store_out<OutT>(a, m, n, red_pos(e));  // a6
+    clear_slots(slots, E, e, a.S);
   }
   publish_flags<RG, OutT>(a, n0, lane);
-  // The tile's counter is zero again for the next launch.
-  if (lane == 0)
-    __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  // Every rank has arrived: the tile's counter is zero again for the next
+  // launch.
+  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   LOWM_TRACE(kTraceEnd);
 }
 
@@ -529,12 +672,8 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
   const int g = lane >> 4;     // which 16-byte vector of a 32-wide K chunk
   const int l16 = lane & 15;   // row within a 16-row MFMA operand
 
-  // a0: blockIdx -> (tile, rank).  Workgroups are dealt to the 8 XCDs
-  // round-robin; the ranks of one tile share blockIdx % 8, hence one XCD.
-  const int bid = (int)blockIdx.x - a.bid_base;
-  const int q = bid / kXcds;
-  const int rank = q % a.S;
-  const int tile = (q / a.S) * kXcds + (bid % kXcds);
+  int tile, rank;
+  decode_tile(a, BN, tile, rank);
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
   if (tile * BN >= a.N) return;
@@ -851,10 +990,8 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
-  const int bid = (int)blockIdx.x - a.bid_base;
-  const int q = bid / kXcds;
-  const int rank = q % a.S;
-  const int tile = (q / a.S) * kXcds + (bid % kXcds);
+  int tile, rank;
+  decode_tile(a, BN, tile, rank);
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
   if (tile * BN >= a.N) return;
@@ -1068,10 +1205,8 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
-  const int bid = (int)blockIdx.x - a.bid_base;
-  const int q = bid / kXcds;
-  const int rank = q % a.S;
-  const int tile = (q / a.S) * kXcds + (bid % kXcds);
+  int tile, rank;
+  decode_tile(a, BN, tile, rank);
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
   if (tile * BN >= a.N) return;
@@ -1225,7 +1360,7 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   // a4: publish (device-scope stores, all acknowledged before the arrival)
   LOWM_STALL(kSitePublish, 0);
   const int E = a.M * BN;
-  float* slots = a.part + (size_t)tile * a.S * E;
+  uint32_t* slots = a.part + (size_t)tile * a.S * E;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -1233,9 +1368,7 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16;
-        if (m < a.M)
-          __hip_atomic_store(slots + (size_t)rank * E + m * BN + nl, sum[rg][b][i],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (m < a.M) store_slot(slots + (size_t)rank * E + m * BN + nl, enc_partial(sum[rg][b][i]));
       }
   wait_vmcnt0();
   pin_issue();
@@ -1251,7 +1384,17 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   }
 
   // a5/a6: the owner folds in rank order (its own partial from registers)
+  // and returns every slot it read to zero
   LOWM_STALL(kSiteFold, 0);
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16;
+        if (m < a.M) sum[rg][b][i] = fold_ranks(slots, E, m * BN + nl, a.S, rank, sum[rg][b][i]);
+      }
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -1260,8 +1403,8 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16, n = n0 + nl;
         if (m >= a.M) continue;
-        const float v = fold_ranks(slots, E, m * BN + nl, a.S, rank, sum[rg][b][i]);
-        if (n < a.N) store_out<OutT>(a, m, n, v);
+        if (n < a.N) store_out<OutT>(a, m, n, sum[rg][b][i]);
+        clear_slots(slots, E, m * BN + nl, a.S);
       }
   publish_flags<RG, OutT>(a, n0, lane);
   if (lane == 0)
@@ -1623,7 +1766,7 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     sl.N = N;
     char* ws = static_cast<char*>(workspace) + ws_off;
     sl.ctr = S > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
-    sl.part = S > 1 ? reinterpret_cast<float*>(ws + counter_bytes(N)) : nullptr;
+    sl.part = S > 1 ? reinterpret_cast<uint32_t*>(ws + counter_bytes(N)) : nullptr;
     ws_off += workspace_bytes(M, N, K, S);
     const size_t tiles = (size_t)((N + BN - 1) / BN);
     grid += round_up(tiles, kXcds) * (size_t)S;

@@ -129,7 +129,7 @@ def test_every_tactic_small_m_ragged_k(lib):
         check_random(lib, wl, tactic=t, what=repr(t))
 
 
-def test_counters_return_to_zero_and_guard_intact(lib):
+def test_workspace_returns_to_zero_and_guard_intact(lib):
     dev = device()
     wl = workloads.HEADLINE
     A, W = inputs(wl)
@@ -143,6 +143,7 @@ def test_counters_return_to_zero_and_guard_intact(lib):
     host = ws.cpu().numpy()
     ctr = host[:sbg.counter_bytes(wl.N)]
     assert not ctr.any(), "an arrival counter was left non-zero"
+    assert not host[:need].any(), "a partial slot was left non-zero"
     assert (host[need:] == 0xA5).all(), "the kernel wrote past the workspace"
 
 
