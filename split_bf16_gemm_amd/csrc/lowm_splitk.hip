@@ -26,16 +26,23 @@
 //  * split_k > 1: every rank stores its fp32 partial in the workspace, makes
 //    it visible at agent scope (release), and counts itself in the tile's
 //    arrival counter with a relaxed atomic.  The rank that sees split_k-1
-//    earlier arrivals is the owner: one acquire fence, then it adds the
-//    partials in rank order 0..split_k-1 (its own from registers, at its own
-//    position), rounds once to bf16 and resets the counter.  Each counter
-//    sits on its own 256-byte line: device-scope atomics on one line are
+//    earlier arrivals is the owner: it reads the peers' partials after the
+//    count (acquire), adds the partials in rank order 0..split_k-1 (its own
+//    from registers, at its own position), rounds once to bf16 and returns
+//    the counter and the tile's partial slots to zero.  A slot word holds the
+//    complement of the partial's bits, so zero means "not published"; the
+//    whole workspace is zero between launches.  Where split_k is 2..4 and a
+//    tile has at most 64 elements, the grid is rank-major and the tile's last
+//    rank polls its peers' slots for a bounded time instead of publishing: a
+//    published slot is visible long before the publisher's acknowledgement
+//    and arrival come back from the loaded memory system.  Each counter sits
+//    on its own 256-byte line: device-scope atomics on one line are
 //    serialised where they execute, so tiles do not share lines.  Scope
 //    matters (PR, Description item 2: a release and an acquire synchronize
 //    only when each one's scope includes the other thread); the acquire is
-//    issued once, on the owner's path only, never in a polling loop (PR,
+//    carried by device-scope loads issued on the owner's path only (PR,
 //    Description item 2, on the cost of an acquiring wait).  No workgroup
-//    waits for another.
+//    waits for another without a bound.
 //
 // Built twice from this source: liblowm.so, and liblowm_stress.so with
 // -DLOWM_STRESS, which adds bounded s_sleep stalls at chosen sites, ranks,
@@ -379,6 +386,16 @@ __device__ __forceinline__ bool early_probe(const Args& a, int BN) {
   return a.S > 1 && a.S - 1 <= kProbeRanks && a.M * BN <= kWave;
 }
 
+// Source of probe load i of a lane: peer i's slot of the lane's element
+// where this wavefront probes and both exist, else a harmless word of A (so
+// that every wavefront can issue the same number of loads).
+__device__ __forceinline__ const uint32_t* probe_src(const Args& a, int E, int tile, int lane,
+                                                     int i, bool probing) {
+  if (probing && i < a.S - 1 && lane < E)
+    return a.part + ((size_t)tile * a.S + i) * E + lane;
+  return reinterpret_cast<const uint32_t*>(a.A);
+}
+
 // a0: workgroup -> (output tile, rank).  Workgroups are dealt to the 8 XCDs
 // round-robin; every rank of a tile gets the same blockIdx % 8, hence one
 // XCD.  Where the early probe applies the order is rank-major: the GEMM's
@@ -478,7 +495,8 @@ __device__ __forceinline__ void publish_flags(const Args& a, int n0, int lane) {
 template <int MB, int RG, typename OutT>
 __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&acc)[RG][MB],
                                                    float* red, int wave, int lane, int tile,
-                                                   int rank, int n0) {
+                                                   int rank, int n0,
+                                                   uint32_t (&probe)[kProbeRanks], bool probed) {
   constexpr int BN = 16 * RG;
   auto red_at = [&](int w, int rg, int b, int i, int ln) -> float& {
     return red[(((w * RG + rg) * MB + b) * 4 + i) * kWave + ln];
@@ -492,20 +510,18 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
       for (int i = 0; i < 4; ++i) red_at(wave, rg, b, i, lane) = acc[rg][b][i];
 
   // Early probe (split_k 2..4, tiles of at most 64 elements): wavefront 0 of
-  // the last rank loads the peers' slots of its element now, so the loads
-  // overlap the wavefront reduction.  Lanes without an element count as
-  // published.
+  // the last rank loads the peers' slots of its element, unless the caller's
+  // main loop already did (`probed`), before the barrier, so the loads
+  // overlap the wavefront reduction.  Words without a peer or an element
+  // count as published.
   const int E = a.M * BN;
   uint32_t* slots = a.part + (size_t)tile * a.S * E;
-  uint32_t probe[kProbeRanks];
-#pragma unroll
-  for (int i = 0; i < kProbeRanks; ++i) probe[i] = 1u;
   const bool probing = early_probe(a, BN) && rank == a.S - 1;
-  if (wave == 0 && probing) {
+  if (wave == 0 && probing && !probed) {
 #pragma unroll
-    for (int i = 0; i < kProbeRanks; ++i)
-      if (i < a.S - 1 && lane < E) probe[i] = load_slot(slots + (size_t)i * E + lane);
+    for (int i = 0; i < kProbeRanks; ++i) probe[i] = load_slot(probe_src(a, E, tile, lane, i, true));
   }
+  auto probe_seen = [&](int i) { return i >= a.S - 1 || lane >= E || probe[i] != 0u; };
 
   // Every wavefront's sums are in LDS after the barrier; wavefront 0 carries
   // on alone.  (A variant where the last wavefront to arrive at an LDS
@@ -556,18 +572,17 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
     for (;;) {
       bool seen = true;
 #pragma unroll
-      for (int i = 0; i < kProbeRanks; ++i) seen = seen && probe[i] != 0u;
+      for (int i = 0; i < kProbeRanks; ++i) seen = seen && probe_seen(i);
       if (__all(seen)) break;
       if (__builtin_amdgcn_s_memrealtime() - t0 > kProbeTicks) break;
       __builtin_amdgcn_s_sleep(2);
 #pragma unroll
       for (int i = 0; i < kProbeRanks; ++i)
-        if (i < a.S - 1 && lane < E && probe[i] == 0u)
-          probe[i] = load_slot(slots + (size_t)i * E + lane);
+        if (!probe_seen(i)) probe[i] = load_slot(slots + (size_t)i * E + lane);
     }
     bool seen = true;
 #pragma unroll
-    for (int i = 0; i < kProbeRanks; ++i) seen = seen && probe[i] != 0u;
+    for (int i = 0; i < kProbeRanks; ++i) seen = seen && probe_seen(i);
     if (__all(seen)) {
       // Every peer has published: this rank is the owner without publishing
       // or arriving.  No peer can become the owner, since only the S-1 peers
@@ -624,14 +639,32 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   // fold is in rank order with this rank's partial, from LDS, at its own
   // position; every slot read goes back to zero.
   LOWM_STALL(kSiteFold, 0);
-  // Two passes: the folds (global loads only, several elements' loads in
+  // Two passes: the folds (global loads only, four elements' loads in
   // flight at once; each result replaces the element's wavefront-0 sum in
   // LDS, which nothing else reads), then the stores of C and the clearing
-  // of the slots, which nothing waits for.
-#pragma unroll 4
-  for (int e = lane; e < E; e += kWave) {
-    const float v = fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
-    red_pos(e) = v;
+  // of the slots, which nothing waits for.  Past the tile's end a lane folds
+  // its first element again and keeps nothing.
+  auto fold_pass = [&](auto sn_c) {
+    constexpr int SN = decltype(sn_c)::value;
+    for (int e0 = lane; e0 < E; e0 += 4 * kWave) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kWave < E ? e0 + u * kWave : e0;
+        v[u] = SN > 0 ? fold_ranks_n<(SN > 0 ? SN : 2)>(slots, E, e, rank, rank_sum(e))
+                      : fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (e0 + u * kWave < E) red_pos(e0 + u * kWave) = v[u];
+    }
+  };
+  switch (a.S) {
+    case 2: fold_pass(std::integral_constant<int, 2>{}); break;
+    case 3: fold_pass(std::integral_constant<int, 3>{}); break;
+    case 4: fold_pass(std::integral_constant<int, 4>{}); break;
+    case 8: fold_pass(std::integral_constant<int, 8>{}); break;
+    default: fold_pass(std::integral_constant<int, 0>{}); break;
   }
   for (int e = lane; e < E; e += kWave) {
     const int m = e / BN, n = n0 + (e - m * BN);
@@ -932,7 +965,8 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
     wait_lgkmcnt0();
     barrier_keep_loads();
   }
-  workgroup_epilogue<MB, RG, OutT>(a, acc, red, wave, lane, tile, rank, n0);
+  uint32_t probe[kProbeRanks];
+  workgroup_epilogue<MB, RG, OutT>(a, acc, red, wave, lane, tile, rank, n0, probe, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1065,11 +1099,31 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
   // Step p (line pair p) out of slot SL: wait until pair p has landed (at
   // most YOUNGER pairs issued after it still in flight), read it, multiply,
   // then refill the slot with pair p+R when REFILL says there is one.
-  auto step = [&](auto slot_c, auto younger_c, int p, bool refill) {
+  // The last rank's probe of its peers' slots (see workgroup_epilogue) is
+  // issued inside the loop, once the second-to-last line pair has landed, so
+  // that its latency overlaps the last pair's.  Every wavefront issues the
+  // same kProbeRanks loads (harmless ones where it does not probe) so the
+  // wait counts stay compile-time constants: after the probe, a step's wait
+  // allows kProbeRanks more outstanding operations.
+  const int E = a.M * BN;
+  const bool probing = early_probe(a, BN) && rank == a.S - 1 && wave == 0;
+  const uint32_t* psrc[kProbeRanks];
+#pragma unroll
+  for (int i = 0; i < kProbeRanks; ++i) psrc[i] = probe_src(a, E, tile, lane, i, probing);
+  uint32_t probe[kProbeRanks];
+  auto issue_probe = [&]() {
+#pragma unroll
+    for (int i = 0; i < kProbeRanks; ++i) probe[i] = load_slot(psrc[i]);
+    pin_issue();
+  };
+  auto step = [&](auto slot_c, auto younger_c, auto extra_c, auto probe_c, int p,
+                  bool refill) {
     constexpr int SL = decltype(slot_c)::value;
     constexpr int YOUNGER = decltype(younger_c)::value;
+    constexpr int EXTRA = decltype(extra_c)::value;
     const u32x4* slot = slot_ptr(slot_c);
-    wait_vmcnt<YOUNGER * G>();
+    wait_vmcnt<YOUNGER * G + EXTRA>();
+    if constexpr (decltype(probe_c)::value) issue_probe();
     LOWM_STALL(kSiteStageRead, p);
     if (p == 0) LOWM_TRACE(kTraceFirstStage);
     // both chunks' W operands (the reads are complete after lds_wait, so the
@@ -1100,11 +1154,12 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
   // R pairs are always in flight and each wait count is the same constant.
   // The first cycle runs before the loop: straight-line code keeps the
   // compiler's own waits for the activation registers exact.
+  using NoProbe = std::false_type;
   auto cycle = [&](int p) {
-    step(I0{}, YR{}, p, true);
-    step(I1{}, YR{}, p + 1, true);
-    if constexpr (R > 2) step(I2{}, YR{}, p + 2, true);
-    if constexpr (R > 3) step(I3{}, YR{}, p + 3, true);
+    step(I0{}, YR{}, I0{}, NoProbe{}, p, true);
+    step(I1{}, YR{}, I0{}, NoProbe{}, p + 1, true);
+    if constexpr (R > 2) step(I2{}, YR{}, I0{}, NoProbe{}, p + 2, true);
+    if constexpr (R > 3) step(I3{}, YR{}, I0{}, NoProbe{}, p + 3, true);
   };
   int p0 = 0;
   if (P >= 2 * R) {
@@ -1134,11 +1189,17 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
     constexpr int I = decltype(i_c)::value;
     if constexpr (I < REM) {
       constexpr int YOUNGER = (REM - 1 - I) < (R - 1) ? (REM - 1 - I) : (R - 1);
-      step(std::integral_constant<int, I % R>{}, std::integral_constant<int, YOUNGER>{}, p0 + I,
+      // the probe goes out after the second-to-last pair's wait (no refill
+      // follows it), so only the last step's wait allows for it
+      constexpr int EXTRA = (I == REM - 1) ? kProbeRanks : 0;
+      constexpr bool PROBE = (REM >= 2 && I == REM - 2);
+      step(std::integral_constant<int, I % R>{}, std::integral_constant<int, YOUNGER>{},
+           std::integral_constant<int, EXTRA>{}, std::integral_constant<bool, PROBE>{}, p0 + I,
            I + R < REM);
     }
   };
   auto tail = [&](auto rem_c) {
+    if constexpr (decltype(rem_c)::value == 1) issue_probe();
     tail_step(rem_c, I0{});
     tail_step(rem_c, I1{});
     tail_step(rem_c, I2{});
@@ -1160,7 +1221,7 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
   }
   mfma_settle(reinterpret_cast<f32x4(&)[RG * MB]>(acc));
   LOWM_TRACE(kTraceLoopEnd);
-  workgroup_epilogue<MB, RG, OutT>(a, acc, red, wave, lane, tile, rank, n0);
+  workgroup_epilogue<MB, RG, OutT>(a, acc, red, wave, lane, tile, rank, n0, probe, true);
 }
 
 template <int MB, int RG, int R, typename OutT>
