@@ -279,6 +279,39 @@ def cpu_baseline(wl, budget_s=10.0):
             "ms_per_call": round(dt * 1e3, 2)}
 
 
+def config_table(lib, dev, steps, reps):
+    """One markdown row per configuration: us/call back-to-back and replayed
+    from a graph, GB/s and % of peak, each W streamed from HBM (rotated pool)."""
+    import torch
+    import workloads
+    print("| workload | tactic | bytes/call | us/call (plain) | us/call (graph) | GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|")
+    for wl in workloads.ALL:
+        M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
+        tac = lib.pick_tactic(M, N, K, S)
+        per_set = 2 * K * N + 2 * M * K + 2 * M * N + lib.workspace_bytes(M, N, K, S)
+        sets = max(2, math.ceil(2 * MALL_BYTES / per_set) + 1)
+        pool = Pool(lib, wl, sets, dev)
+        call = make_caller(lib, wl, None, torch.cuda.current_stream(dev).cuda_stream)
+        for i in range(20):
+            call(pool.ptrs[i % sets])
+        torch.cuda.synchronize()
+        us = statistics.median(time_loop(call, pool.ptrs, steps) for _ in range(reps))
+        try:
+            ug = statistics.median(
+                time_graph(lambda h: make_caller(lib, wl, None, h), pool.ptrs, steps, dev)
+                for _ in range(reps))
+        except Exception:  # graph capture is an extra figure
+            ug = float("nan")
+        nbytes = algorithmic_bytes(M, N, K, S)
+        gbps = nbytes / us / 1e3
+        stage = repr(tac).split("(")[1].split(",")[0]
+        print(f"| {wl.name} | {stage}:{tac.rows}:{tac.unroll}:{tac.stages} | {nbytes:,} | "
+              f"{us:.2f} | {ug:.2f} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f} |", flush=True)
+        del pool
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +326,9 @@ def main():
                     help="no GPU: write the HBM traffic record from four rocprofv3 --pmc "
                          "output directories (FETCH_SIZE, WRITE_SIZE of this bench, then of "
                          "--calibrate-copy)")
+    ap.add_argument("--table", action="store_true",
+                    help="time every configuration (plain loop and graph replay, weights "
+                         "from HBM) and print a markdown table instead of the JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy kernel (50,331,648 bytes per launch) so "
                          "profiler byte counters can be scaled against a known size")
@@ -320,6 +356,9 @@ def main():
         calibrate_copy(dev, args.steps)
         return
     lib = sbg.load()
+    if args.table:
+        config_table(lib, dev, args.steps, args.reps)
+        return
     wl = workloads.by_name(args.workload)
     M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
     tactic = parse_tactic(args.tactic)

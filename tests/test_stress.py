@@ -116,3 +116,49 @@ def test_stress_library_without_stalls_matches(libs):
     ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
     say("stress lib, no stalls")
     assert np.array_equal(launch(base, (A, W, ws), wl, None), launch(stress, (A, W, ws), wl, None))
+
+
+def _early_owners(stress, ops, wl):
+    """Tiles whose last rank folded without arriving, from the stress build's
+    per-workgroup timestamp trace of one launch (such a rank records an end
+    but no arrival).  A traced launch measures timing only: its timestamp
+    stores share the wait counter with the weight loads, so its output is
+    not checked."""
+    A, W, ws = ops
+    tiles = (wl.N + 15) // 16
+    grid = (tiles + 7) // 8 * 8 * wl.split_k
+    buf = torch.zeros(grid * 8, dtype=torch.int64, device=A.device)
+    stress.trace(buf)
+    try:
+        stress.gemm(A, W, wl.split_k, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        stress.trace(None)
+    tr = buf.view(grid, 8).cpu().numpy()
+    return int(((tr[:, 5] > 0) & (tr[:, 4] == 0)).sum())
+
+
+def test_last_rank_folds_early_and_its_poll_gives_up(libs):
+    """At the headline shape the tile's last rank polls its peer's slot and,
+    once the partial is there, folds without publishing or arriving.  With
+    rank 0's publish stalled 100 us, past the poll's 20 us limit, no tile
+    takes that path (the last rank publishes and arrives instead, and rank 0
+    becomes the owner), and the output is unchanged bit for bit."""
+    base, stress = libs
+    wl = workloads.HEADLINE
+    dev = device()
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    ops = (A, W, ws)
+    say("early owner trace, no stall")
+    ref = launch(base, ops, wl, None)
+    assert _early_owners(stress, ops, wl) > 0, "no tile took the early-owner path"
+    stress.configure_stress(binding.SITE_PUBLISH, 0, -1, 0, 0, -1, 100_000)
+    try:
+        say("early owner trace, rank 0 publish stalled 100 us")
+        assert _early_owners(stress, ops, wl) == 0, "a last rank folded without its peer's partial"
+        got = launch(stress, ops, wl, None)
+    finally:
+        stress.configure_stress(0)
+    assert np.array_equal(got, ref), "the poll's time-out path changed the output"
+    assert not ws.cpu().numpy().any(), "the workspace was left non-zero"
