@@ -104,9 +104,10 @@ size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k);
  * Batched launch: `count` (1 .. LOWM_MAX_BATCH) independent products
  * C_g = A_g * W_g^T that share M, K, split_k and the bf16 output, in one
  * kernel launch (one launch gap instead of `count`; the GEMMs' tails
- * overlap).  Each GEMM is exactly what lowm_gemm_splitk computes for it, with
- * the same tactic (the default for M, K, split_k), so its output is bitwise
- * the single call's.  The workspace (split_k > 1) is the concatenation, in
+ * overlap).  Each GEMM is exactly what lowm_gemm_splitk computes for it: one
+ * tactic serves the launch (the default for M, K, split_k and the narrowest
+ * N_g), whose per-element summation order equals the single call's, so each
+ * output is bitwise the single call's.  The workspace (split_k > 1) is the concatenation, in
  * order, of each GEMM's own workspace of lowm_gemm_splitk_workspace_bytes
  * (M, N_g, K, split_k) bytes; lowm_gemm_splitk_batched_workspace_bytes gives
  * the total.  Zero it once; every completed launch leaves it reusable.

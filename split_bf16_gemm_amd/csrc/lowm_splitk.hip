@@ -1634,7 +1634,6 @@ size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
 int pick(int M, int N, int K, int S, lowm_tactic* t) {
   const int rc = check_sizes(M, N, K, S);
   if (rc != LOWM_OK) return rc;
-  (void)N;
   const int nvec = K / S / kVecK;
   const int cpw = ((nvec + 3) / 4 + kWaves - 1) / kWaves;
   const int act = (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) ? 1 : 0;
@@ -1663,6 +1662,15 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
   };
   if (nvec % 32 == 0 && M <= 32) {
     const int pairs = nvec / 32;   // line pairs per wavefront
+    // Measured on MI355X: 32-row line tiles beat 16-row ones only without
+    // split-K, for 5..16 activation rows, 16 line pairs per wavefront and at
+    // least 192 tiles (M 16, N 6144, K 4096: 12.3 vs 14.4 us; M 16, N 24576:
+    // 32.9 vs 40.5); with split_k 2..8, other slice lengths or fewer tiles
+    // they lose.
+    if (S == 1 && M > 4 && M <= 16 && pairs == 16 && (N + 31) / 32 >= 192) {
+      t->rows = 32;
+      if (provides({kStageLine, 2, 2})) return LOWM_OK;
+    }
     if (!(M > 16 && pairs >= 16)) {
       const int ring = (M <= 4 && pairs >= 8 && pairs < 16) ? 4 : 2;
       t->rows = 16;
@@ -1807,7 +1815,11 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
   if (tactic) {
     t = *tactic;
   } else {
-    rc = pick(M, gemms[0].N, K, S, &t);
+    // One tactic serves every GEMM of the launch: pick it for the narrowest
+    // (the only rule that depends on N asks for enough tiles).
+    int n_min = gemms[0].N;
+    for (int g = 1; g < count; ++g) n_min = gemms[g].N < n_min ? gemms[g].N : n_min;
+    rc = pick(M, n_min, K, S, &t);
     if (rc != LOWM_OK) return rc;
   }
   const int nvec = K / S / kVecK;

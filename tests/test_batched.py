@@ -22,6 +22,8 @@ CASES = [
     (4, [1024, 2048], 1024, 1),            # split_k 1: no workspace
     (1, [6144] * 8, 4096, 8),              # the largest batch
     (4, [768], 4096, 2),                   # a batch of one
+    (8, [6144, 6144], 4096, 1),            # 32-row line tiles for every GEMM
+    (8, [6144, 1024], 4096, 1),            # 16-row tiles for the batch, 32-row alone
 ]
 
 
