@@ -170,3 +170,28 @@ def test_launch_is_asynchronous_on_the_given_stream(lib):
     s.synchronize()
     C, S = oracle_result(wl)
     assert_fp32(out.cpu().numpy(), C, S)
+
+
+def test_one_workspace_serves_launches_of_different_shapes(lib):
+    """Every launch returns the whole workspace to zero, so one buffer, sized
+    for the largest shape, serves launches of any shape in turn, early-owner
+    shapes (the last rank reads its peers' slots without the counter) after
+    counter-only ones and back, each bit-identical to a launch on a fresh
+    workspace."""
+    dev = device()
+    shapes = [workloads.Workload("ws_a", 4, 6144, 4096, 2, seed_a=31, seed_w=32),
+              workloads.Workload("ws_b", 16, 2304, 4096, 8, seed_a=33, seed_w=34),
+              workloads.Workload("ws_c", 2, 1000, 3072, 3, seed_a=35, seed_w=36),
+              workloads.Workload("ws_d", 64, 768, 2048, 4, seed_a=37, seed_w=38)]
+    need = max(lib.workspace_bytes(w.M, w.N, w.K, w.split_k) for w in shapes)
+    shared = torch.zeros(need, dtype=torch.uint8, device=dev)
+    fresh = {}
+    for wl in shapes:
+        A, W = inputs(wl)
+        fresh[wl.name] = to_bits(run(lib, A, W, wl.split_k))
+    say("shared workspace, mixed shapes")
+    for wl in shapes + shapes[::-1]:
+        A, W = inputs(wl)
+        got = to_bits(run(lib, A, W, wl.split_k, workspace=shared))
+        assert np.array_equal(got, fresh[wl.name]), f"{wl.name} differs on the shared workspace"
+        assert not shared.cpu().numpy().any(), f"{wl.name} left the shared workspace non-zero"
