@@ -1,8 +1,8 @@
 """Batched launches: several independent GEMMs that share M, K and split_k in
 one kernel launch.  Each GEMM of a batch must equal, bit for bit, the single
 launch of the same product (same kernel, same summation order); the first one
-is also judged against the oracle, and every counter of the workspace must be
-zero again afterwards."""
+is also judged against the oracle, and the whole workspace (counters and
+partial slots) must be zero again afterwards."""
 from __future__ import annotations
 
 import numpy as np
