@@ -172,6 +172,50 @@ def hbm_read_ceiling(pool, dev, reps=5):
     return statistics.median(res)
 
 
+def read_mall_warm(W, dev, steps, reps=5):
+    """us per launch of the plain streaming read over one W again and again
+    (the Infinity Cache holds it: not an HBM figure)."""
+    import torch
+    from split_bf16_gemm_amd import BwProbe
+    bw = BwProbe()
+    blocks = 1024
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    for _ in range(20):
+        bw.read(W, sink, blocks)
+    res = []
+    for _ in range(reps):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            bw.read(W, sink, blocks)
+        end.record()
+        end.synchronize()
+        res.append(start.elapsed_time(end) * 1e3 / steps)
+    return statistics.median(res)
+
+
+def launch_floor(blocks, steps, reps=5):
+    """us per launch of back-to-back empty kernels with `blocks` workgroups of
+    256 threads: the fixed cost of a launch of the GEMM's grid."""
+    import torch
+    from split_bf16_gemm_amd import BwProbe
+    bw = BwProbe()
+    for _ in range(20):
+        bw.empty(blocks)
+    res = []
+    for _ in range(reps):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            bw.empty(blocks)
+        end.record()
+        end.synchronize()
+        res.append(start.elapsed_time(end) * 1e3 / steps)
+    return statistics.median(res)
+
+
 def pmc_traffic(wl, tactic_dict, launches_bytes):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -388,6 +432,9 @@ def main():
         except Exception as e:  # graph capture is an extra figure, not the metric
             log(f"graph timing skipped: {e}")
     ceiling = hbm_read_ceiling(pool, dev)
+    grid = (-(-N // tac.rows) + 7) // 8 * 8 * S      # the GEMM's workgroups
+    floor_us = launch_floor(grid, args.steps)
+    read_warm_us = read_mall_warm(pool.sets[0][1], dev, args.steps)
 
     nbytes = algorithmic_bytes(M, N, K, S)
     gbps = nbytes / us_loop / 1e3
@@ -397,7 +444,7 @@ def main():
     achieved = gbps
     log(f"us/call {us_loop:.3f} (plain loop), kernel {us_kernel:.3f} avg / {us_kernel_med:.3f} "
         f"median (event pairs), graph {us_graph}, MALL-warm {us_warm:.3f}; "
-        f"HBM read ceiling {ceiling:.0f} GB/s")
+        f"HBM read ceiling {ceiling:.0f} GB/s; empty kernel, {grid} workgroups: {floor_us:.3f} us")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
     out = {
@@ -426,6 +473,8 @@ def main():
             "kernel_median_event_pairs": round(us_kernel_med, 3),
             "graph_replay_per_call": None if us_graph is None else round(us_graph, 3),
             "mall_warm_single_set_not_hbm": round(us_warm, 3),
+            "empty_kernel_same_grid": round(floor_us, 3),
+            "plain_read_mall_warm_not_hbm": round(read_warm_us, 3),
         },
         "hbm_read_ceiling_gbps": round(ceiling, 1),
         "roofline": {

@@ -369,7 +369,14 @@ class BwProbe:
         lib.bwprobe_read.restype = _i
         lib.bwprobe_copy.argtypes = [_vp, _vp, ctypes.c_size_t, _i, _vp]
         lib.bwprobe_copy.restype = _i
+        lib.bwprobe_empty.argtypes = [_i, _vp]
+        lib.bwprobe_empty.restype = _i
         self.lib = lib
+
+    def empty(self, blocks: int):
+        rc = self.lib.bwprobe_empty(blocks, torch.cuda.current_stream().cuda_stream)
+        if rc:
+            raise RuntimeError(f"bwprobe_empty failed: hipError {rc}")
 
     def read(self, src: torch.Tensor, sink: torch.Tensor, blocks: int):
         n = src.numel() * src.element_size()

@@ -1,6 +1,7 @@
 // bwprobe.hip -- plain streaming kernels that measure the HBM ceiling of the
-// device they run on, and a copy of known size whose profiler byte counters
-// calibrate the counters of the GEMM kernel.  Not part of the GEMM path.
+// device they run on, a copy of known size whose profiler byte counters
+// calibrate the counters of the GEMM kernel, and an empty kernel that times
+// the fixed cost of a launch.  Not part of the GEMM path.
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -40,6 +41,11 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src
     dst[i] = src[i];
 }
 
+// Does nothing.  Back-to-back launches of it with the GEMM's grid time the
+// fixed cost of a launch of that shape (dispatch, workgroup start and end,
+// the end-of-kernel release), below which no kernel of that grid can go.
+__global__ __launch_bounds__(256) void empty_kernel() {}
+
 }  // namespace
 
 extern "C" {
@@ -58,6 +64,14 @@ int bwprobe_copy(const void* src, void* dst, size_t bytes, int blocks, void* str
   if (!src || !dst || bytes % 16 || blocks <= 0) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  return (int)hipGetLastError();
+}
+
+// Launches the empty kernel with `blocks` workgroups of 256 threads.
+// Returns a hipError_t.
+int bwprobe_empty(int blocks, void* stream) {
+  if (blocks <= 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(empty_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream));
   return (int)hipGetLastError();
 }
 
