@@ -195,21 +195,30 @@ def read_mall_warm(W, dev, steps, reps=5):
     return statistics.median(res)
 
 
-def launch_floor(blocks, steps, reps=5):
-    """us per launch of back-to-back empty kernels with `blocks` workgroups of
-    256 threads: the fixed cost of a launch of the GEMM's grid."""
+def launch_floor(blocks, steps, dev, reps=5):
+    """us per launch of `steps` empty kernels with `blocks` workgroups of 256
+    threads, captured in one graph and replayed: the GPU's fixed cost of a
+    launch of the GEMM's grid.  (Issued one by one from Python, each launch
+    costs the host more than the GPU, so a plain loop would time the host.)"""
     import torch
     from split_bf16_gemm_amd import BwProbe
     bw = BwProbe()
-    for _ in range(20):
-        bw.empty(blocks)
+    s = torch.cuda.Stream(device=dev)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(steps):
+            rc = bw.lib.bwprobe_empty(blocks, s.cuda_stream)
+            if rc:
+                raise RuntimeError(f"bwprobe_empty failed: hipError {rc}")
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
     res = []
     for _ in range(reps):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         start.record()
-        for _ in range(steps):
-            bw.empty(blocks)
+        g.replay()
         end.record()
         end.synchronize()
         res.append(start.elapsed_time(end) * 1e3 / steps)
@@ -433,7 +442,7 @@ def main():
             log(f"graph timing skipped: {e}")
     ceiling = hbm_read_ceiling(pool, dev)
     grid = (-(-N // tac.rows) + 7) // 8 * 8 * S      # the GEMM's workgroups
-    floor_us = launch_floor(grid, args.steps)
+    floor_us = launch_floor(grid, args.steps, dev)
     read_warm_us = read_mall_warm(pool.sets[0][1], dev, args.steps)
 
     nbytes = algorithmic_bytes(M, N, K, S)
@@ -473,7 +482,7 @@ def main():
             "kernel_median_event_pairs": round(us_kernel_med, 3),
             "graph_replay_per_call": None if us_graph is None else round(us_graph, 3),
             "mall_warm_single_set_not_hbm": round(us_warm, 3),
-            "empty_kernel_same_grid": round(floor_us, 3),
+            "empty_kernel_same_grid_graph": round(floor_us, 3),
             "plain_read_mall_warm_not_hbm": round(read_warm_us, 3),
         },
         "hbm_read_ceiling_gbps": round(ceiling, 1),
