@@ -109,6 +109,22 @@ def test_pick_prefers_line_pairs_where_measured_faster(lib):
     assert t.stage != line
 
 
+def test_pick_32_row_line_tiles_only_where_measured_faster(lib):
+    """32-row line tiles: split_k 1, 5..16 rows, 16 line pairs per wavefront
+    and at least 192 tiles; 16-row tiles otherwise."""
+    line = binding.LOWM_STAGE_LINE
+    for M, N, K, S, rows in [(16, 6144, 4096, 1, 32), (8, 6144, 4096, 1, 32),
+                             (5, 24576, 4096, 1, 32), (12, 6144, 4096, 1, 32),
+                             (16, 6144, 4096, 2, 16),    # split-K
+                             (4, 6144, 4096, 1, 16),     # M <= 4
+                             (16, 768, 4096, 1, 16),     # 24 tiles
+                             (16, 6080, 4096, 1, 16),    # 190 tiles
+                             (16, 6144, 8192, 1, 16),    # 32 pairs
+                             (16, 6144, 2048, 1, 16)]:   # 8 pairs
+        t = lib.pick_tactic(M, N, K, S)
+        assert (t.stage, t.rows) == (line, rows), (M, N, K, S, t)
+
+
 def call(lib, A=FAKE, W=FAKE, C=FAKE, M=4, N=64, K=256, S=2, ws=FAKE, f32=False, tac=None):
     return lib.call_raw(A, W, C, M, N, K, S, ws, 0, f32out=f32, tactic=tac)
 
