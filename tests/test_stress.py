@@ -162,3 +162,27 @@ def test_last_rank_folds_early_and_its_poll_gives_up(libs):
         stress.configure_stress(0)
     assert np.array_equal(got, ref), "the poll's time-out path changed the output"
     assert not ws.cpu().numpy().any(), "the workspace was left non-zero"
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2])
+def test_split_k4_poll_gives_up_on_a_stalled_middle_rank(libs, rank):
+    """split_k 4 (N 2304, K 12288): the last rank polls three peers.  One peer
+    rank, on every other tile, stalls 100 us before publishing: the poll
+    gives up after 20 us, the last rank publishes and arrives, and the
+    stalled rank, arriving last, folds.  Tiles without the stall take the
+    early path.  Every output bit must match the unstalled launch."""
+    base, stress = libs
+    wl = workloads.SPLITK4
+    dev = device()
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    ops = (A, W, ws)
+    say("split_k 4, stalled publish of rank", rank)
+    ref = launch(base, ops, wl, None)
+    stress.configure_stress(binding.SITE_PUBLISH, rank, -1, 2, 1, -1, 100_000)
+    try:
+        got = launch(stress, ops, wl, None)
+    finally:
+        stress.configure_stress(0)
+    assert np.array_equal(got, ref), f"stalled rank {rank}: output differs"
+    assert not ws.cpu().numpy().any(), "the workspace was left non-zero"
