@@ -1693,16 +1693,16 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
 // K is long; for M 16 the larger partials make it pay less often.
 constexpr unsigned char kBestSplit[2][6][4] = {
     // M <= 8            K: 2048 4096 8192 16384
-    {{1, 8, 8, 8},    // N 768
-     {1, 8, 8, 8},    // N 1536
-     {1, 8, 4, 4},    // N 3072
-     {1, 1, 2, 8},    // N 6144
-     {1, 1, 4, 8},    // N 12288
-     {1, 1, 4, 8}},   // N 24576
+    {{1, 4, 4, 8},    // N 768
+     {2, 2, 4, 4},    // N 1536
+     {1, 2, 2, 4},    // N 3072
+     {1, 2, 2, 8},    // N 6144
+     {1, 1, 2, 8},    // N 12288
+     {1, 1, 2, 8}},   // N 24576
     // M > 8
-    {{1, 4, 8, 4},
-     {1, 1, 8, 8},
-     {1, 1, 1, 4},
+    {{1, 4, 4, 4},
+     {1, 2, 8, 8},
+     {1, 1, 4, 4},
      {1, 1, 2, 4},
      {1, 1, 1, 1},
      {1, 1, 1, 1}}};

@@ -216,11 +216,13 @@ def test_line_tactic_needs_whole_line_pairs(lib):
 
 def test_pick_split_k(lib):
     # the measured table at its grid points (MI355X, default tactic per split_k)
-    assert lib.pick_split_k(4, 6144, 4096) == 1
+    assert lib.pick_split_k(4, 6144, 4096) == 2
     assert lib.pick_split_k(4, 6144, 8192) == 2
-    assert lib.pick_split_k(4, 768, 4096) == 8
+    assert lib.pick_split_k(4, 768, 4096) == 4
     assert lib.pick_split_k(4, 3072, 16384) == 4
+    assert lib.pick_split_k(4, 12288, 4096) == 1
     assert lib.pick_split_k(16, 768, 4096) == 4
+    assert lib.pick_split_k(16, 6144, 4096) == 1
     assert lib.pick_split_k(16, 24576, 16384) == 1
     # always a split_k the launch accepts
     for M in (1, 4, 9, 16, 33, 64):
