@@ -32,12 +32,16 @@ if str(ROOT) not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 MALL_BYTES = 256 << 20          # Infinity Cache
-KERNEL_SOURCE = ROOT / "split_bf16_gemm_amd" / "csrc" / "lowm_splitk.hip"
+KERNEL_SOURCES = ROOT / "split_bf16_gemm_amd" / "csrc"
 PMC_FILE = ROOT / "profiles" / "pmc_traffic.json"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def rnd(x, nd):
+    return None if x is None else round(x, nd)
 
 
 def algorithmic_bytes(M: int, N: int, K: int, S: int) -> int:
@@ -48,7 +52,12 @@ def algorithmic_bytes(M: int, N: int, K: int, S: int) -> int:
 
 
 def source_hash() -> str:
-    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()[:16]
+    """Hash of the GEMM library's sources (the kernels and the host side)."""
+    h = hashlib.sha256()
+    for f in sorted(KERNEL_SOURCES.glob("lowm_*")) + [ROOT / "include" / "lowm.h"]:
+        h.update(f.name.encode())
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
 
 
 def parse_tactic(text):
@@ -309,6 +318,31 @@ def summarize_pmc(wl_name: str, tactic_text, fetch: Path, write: Path, cfetch: P
     return rec
 
 
+def counter_summary(dirs, kernel_filter="lowm_"):
+    """Markdown table of the median per-dispatch value of every counter in
+    rocprofv3 --pmc output directories, per kernel whose name contains
+    kernel_filter (no GPU needed)."""
+    import csv
+    rows: dict = {}
+    for d in dirs:
+        for f in sorted(Path(d).rglob("*counter_collection.csv")):
+            with open(f, newline="") as fh:
+                for row in csv.DictReader(fh):
+                    k = row.get("Kernel_Name", "")
+                    if kernel_filter not in k:
+                        continue
+                    k = k.split("(")[0]
+                    rows.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(
+                        float(row["Counter_Value"]))
+    for k, counters in rows.items():
+        print(f"\n**{k}**\n")
+        print("| counter | median per dispatch | dispatches |")
+        print("|---|---|---|")
+        for c in sorted(counters):
+            v = counters[c]
+            print(f"| {c} | {statistics.median(v):,.0f} | {len(v)} |")
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The fp64 oracle on the host cores: full products of the workload,
     repeated until about budget_s seconds of CPU work."""
@@ -365,6 +399,84 @@ def config_table(lib, dev, steps, reps):
         torch.cuda.empty_cache()
 
 
+def time_shape(lib, dev, M, N, K, S, tactic, steps, reps, seed=0):
+    """us/call of back-to-back launches of one shape and tactic (None: the
+    default), W streamed from HBM through a rotated pool of synthetic input
+    sets larger than twice the MALL; median of `reps` timed loops.  Returns
+    None when the build has no such tactic for the shape."""
+    import torch
+    import workloads
+    from split_bf16_gemm_amd import binding
+    if lib.check_launch(M, N, K, S, tactic=tactic) != binding.LOWM_OK:
+        return None
+    wl = workloads.Workload(f"shape_m{M}_n{N}_k{K}_s{S}", M, N, K, S,
+                            seed_a=3000 + seed, seed_w=4000 + seed)
+    per_set = 2 * K * N + 2 * M * K + 2 * M * N + lib.workspace_bytes(M, N, K, S)
+    sets = max(2, math.ceil(2 * MALL_BYTES / per_set) + 1)
+    pool = Pool(lib, wl, sets, dev)
+    call = make_caller(lib, wl, tactic, torch.cuda.current_stream(dev).cuda_stream)
+    for i in range(max(10, sets)):
+        call(pool.ptrs[i % sets])
+    torch.cuda.synchronize()
+    us = statistics.median(time_loop(call, pool.ptrs, steps) for _ in range(reps))
+    del pool
+    torch.cuda.empty_cache()
+    return us
+
+
+def tactic_text(t) -> str:
+    stage = repr(t).split("(")[1].split(",")[0]
+    return f"{stage}:{t.rows}:{t.unroll}:{t.stages}"
+
+
+def tactic_matrix(lib, dev, workload_names, tactic_texts, steps, reps):
+    """Markdown table: us/call (and % of 8 TB/s) of every listed tactic on
+    every listed workload ('default' is the tactic lowm_pick_tactic gives)."""
+    import workloads
+    print("| workload | " + " | ".join(tactic_texts) + " | best |")
+    print("|---|" + "---|" * (len(tactic_texts) + 1))
+    for name in workload_names:
+        wl = workloads.by_name(name)
+        M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
+        nbytes = algorithmic_bytes(M, N, K, S)
+        cells, best = [], None
+        for text in tactic_texts:
+            t = None if text == "default" else parse_tactic(text)
+            us = time_shape(lib, dev, M, N, K, S, t, steps, reps)
+            if us is None:
+                cells.append("—")
+                continue
+            label = text if t is not None else f"default ({tactic_text(lib.pick_tactic(M, N, K, S))})"
+            if best is None or us < best[0]:
+                best = (us, label)
+            cells.append(f"{us:.2f} ({100 * nbytes / us / 1e3 / PEAK_HBM_GBPS:.1f} %)")
+        print(f"| {name} | " + " | ".join(cells) + f" | {best[1] if best else '—'} |", flush=True)
+
+
+SPLIT_GRID = {"M": (4, 16, 32, 64), "N": (768, 1536, 3072, 6144, 12288, 24576),
+              "K": (2048, 4096, 8192, 16384), "S": (1, 2, 4, 8)}
+
+
+def split_sweep(lib, dev, Ms, steps, reps):
+    """For each (M, N, K) of the grid: us/call with the default tactic at
+    split_k 1, 2, 4, 8, the fastest split_k, and what lowm_pick_split_k says."""
+    print("| M | N | K | " + " | ".join(f"split_k {s}" for s in SPLIT_GRID["S"]) +
+          " | fastest | picked |")
+    print("|---|---|---|" + "---|" * (len(SPLIT_GRID["S"]) + 2))
+    for M in Ms:
+        for N in SPLIT_GRID["N"]:
+            for K in SPLIT_GRID["K"]:
+                times = {}
+                for S in SPLIT_GRID["S"]:
+                    us = time_shape(lib, dev, M, N, K, S, None, steps, reps, seed=S)
+                    if us is not None:
+                        times[S] = us
+                best = min(times, key=times.get)
+                cells = [f"{times[S]:.2f}" if S in times else "—" for S in SPLIT_GRID["S"]]
+                print(f"| {M} | {N} | {K} | " + " | ".join(cells) +
+                      f" | {best} | {lib.pick_split_k(M, N, K)} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,13 +487,25 @@ def main():
     ap.add_argument("--reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--only-gemm", action="store_true",
+                    help="time only the GEMM loop (for profiler runs): no event pairs, graph, "
+                         "MALL-warm, read ceiling or launch floor figures")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
                     help="no GPU: write the HBM traffic record from four rocprofv3 --pmc "
                          "output directories (FETCH_SIZE, WRITE_SIZE of this bench, then of "
                          "--calibrate-copy)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="no GPU: print the median per-dispatch value of every counter in "
+                         "these rocprofv3 --pmc output directories, per GEMM kernel")
     ap.add_argument("--table", action="store_true",
                     help="time every configuration (plain loop and graph replay, weights "
                          "from HBM) and print a markdown table instead of the JSON line")
+    ap.add_argument("--tactic-matrix", nargs=2, metavar=("WORKLOADS", "TACTICS"),
+                    help="comma-separated workload names and tactics (stage:rows:unroll:stages "
+                         "or 'default'): print a markdown table of us/call, W from HBM")
+    ap.add_argument("--split-sweep", metavar="MS",
+                    help="comma-separated M values: time split_k 1/2/4/8 with the default "
+                         "tactic over the N x K grid and print the fastest per shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy kernel (50,331,648 bytes per launch) so "
                          "profiler byte counters can be scaled against a known size")
@@ -390,6 +514,10 @@ def main():
     if args.summarize_pmc:
         rec = summarize_pmc(args.workload, args.tactic, *(Path(d) for d in args.summarize_pmc))
         print(json.dumps(rec), flush=True)
+        return
+
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
 
     if args.gpus != 1:
@@ -412,6 +540,13 @@ def main():
     if args.table:
         config_table(lib, dev, args.steps, args.reps)
         return
+    if args.tactic_matrix:
+        names, tacs = (x.split(",") for x in args.tactic_matrix)
+        tactic_matrix(lib, dev, names, tacs, args.steps, args.reps)
+        return
+    if args.split_sweep:
+        split_sweep(lib, dev, [int(m) for m in args.split_sweep.split(",")], args.steps, args.reps)
+        return
     wl = workloads.by_name(args.workload)
     M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
     tactic = parse_tactic(args.tactic)
@@ -428,22 +563,25 @@ def main():
     torch.cuda.synchronize()
 
     us_loop = statistics.median(time_loop(call, pool.ptrs, args.steps) for _ in range(args.reps))
-    each = [time_each(call, pool.ptrs, args.steps) for _ in range(args.reps)]
-    us_kernel = statistics.median(e[0] for e in each)
-    us_kernel_med = statistics.median(e[1] for e in each)
-    us_warm = statistics.median(time_loop(call, pool.ptrs[:1], args.steps) for _ in range(args.reps))
-    us_graph = None
-    if not args.no_graph:
-        try:
-            us_graph = statistics.median(
-                time_graph(lambda h: make_caller(lib, wl, tactic, h), pool.ptrs, args.steps, dev)
-                for _ in range(args.reps))
-        except Exception as e:  # graph capture is an extra figure, not the metric
-            log(f"graph timing skipped: {e}")
-    ceiling = hbm_read_ceiling(pool, dev)
     grid = (-(-N // tac.rows) + 7) // 8 * 8 * S      # the GEMM's workgroups
-    floor_us = launch_floor(grid, args.steps, dev)
-    read_warm_us = read_mall_warm(pool.sets[0][1], dev, args.steps)
+    us_kernel = us_kernel_med = us_warm = us_graph = ceiling = floor_us = read_warm_us = None
+    if not args.only_gemm:
+        each = [time_each(call, pool.ptrs, args.steps) for _ in range(args.reps)]
+        us_kernel = statistics.median(e[0] for e in each)
+        us_kernel_med = statistics.median(e[1] for e in each)
+        us_warm = statistics.median(time_loop(call, pool.ptrs[:1], args.steps)
+                                    for _ in range(args.reps))
+        if not args.no_graph:
+            try:
+                us_graph = statistics.median(
+                    time_graph(lambda h: make_caller(lib, wl, tactic, h), pool.ptrs, args.steps,
+                               dev)
+                    for _ in range(args.reps))
+            except Exception as e:  # graph capture is an extra figure, not the metric
+                log(f"graph timing skipped: {e}")
+        ceiling = hbm_read_ceiling(pool, dev)
+        floor_us = launch_floor(grid, args.steps, dev)
+        read_warm_us = read_mall_warm(pool.sets[0][1], dev, args.steps)
 
     nbytes = algorithmic_bytes(M, N, K, S)
     gbps = nbytes / us_loop / 1e3
@@ -451,9 +589,9 @@ def main():
     # (the profiler's per-kernel average agrees within the launch gap); event
     # pairs around every launch add several microseconds of their own.
     achieved = gbps
-    log(f"us/call {us_loop:.3f} (plain loop), kernel {us_kernel:.3f} avg / {us_kernel_med:.3f} "
-        f"median (event pairs), graph {us_graph}, MALL-warm {us_warm:.3f}; "
-        f"HBM read ceiling {ceiling:.0f} GB/s; empty kernel, {grid} workgroups: {floor_us:.3f} us")
+    log(f"us/call {us_loop:.3f} (plain loop), kernel {us_kernel} avg / {us_kernel_med} "
+        f"median (event pairs), graph {us_graph}, MALL-warm {us_warm}; "
+        f"HBM read ceiling {ceiling} GB/s; empty kernel, {grid} workgroups: {floor_us} us")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
     out = {
@@ -478,14 +616,14 @@ def main():
         },
         "timings_us": {
             "plain_loop_per_call": round(us_loop, 3),
-            "kernel_avg_event_pairs": round(us_kernel, 3),
-            "kernel_median_event_pairs": round(us_kernel_med, 3),
-            "graph_replay_per_call": None if us_graph is None else round(us_graph, 3),
-            "mall_warm_single_set_not_hbm": round(us_warm, 3),
-            "empty_kernel_same_grid_graph": round(floor_us, 3),
-            "plain_read_mall_warm_not_hbm": round(read_warm_us, 3),
+            "kernel_avg_event_pairs": rnd(us_kernel, 3),
+            "kernel_median_event_pairs": rnd(us_kernel_med, 3),
+            "graph_replay_per_call": rnd(us_graph, 3),
+            "mall_warm_single_set_not_hbm": rnd(us_warm, 3),
+            "empty_kernel_same_grid_graph": rnd(floor_us, 3),
+            "plain_read_mall_warm_not_hbm": rnd(read_warm_us, 3),
         },
-        "hbm_read_ceiling_gbps": round(ceiling, 1),
+        "hbm_read_ceiling_gbps": rnd(ceiling, 1),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

@@ -144,38 +144,46 @@ int lowm_last_hip_error(void);
  * (M, N, K, split_k); the _ex entry points take it explicitly, for tuning
  * sweeps and for tests that cover every variant.  Any tactic gives a correct
  * result; the summation order (and so the low bits of random-input results)
- * depends on it.
- *   stage      LOWM_STAGE_LDS: W goes global -> an LDS ring of `stages`
- *              stages shared by the workgroup; a stage holds 512 K of each of
- *              the tile's rows, each direct-to-LDS load moving 1 KB of one row;
- *              a stage is refilled only after a workgroup barrier that every
- *              wavefront reaches once its reads of it are done.  unroll must
- *              be 4.  LOWM_STAGE_REG: W goes global -> registers, a ring of
- *              `stages` register stages per wavefront, `unroll` 32-wide K
- *              chunks per wavefront per stage; each wavefront streams its
- *              own contiguous quarter of the K slice.
- *              LOWM_STAGE_WAVE: a workgroup is one wavefront that owns its
- *              tile for the whole K slice; W goes global -> a ring of `stages`
- *              register stages of `unroll` chunks; no barriers at all.
- *              LOWM_STAGE_LINE: W goes global -> LDS in whole 128-byte lines
+ * depends on it.  The pages ship fixed tactics per split_k (TensorRT-LLM PR
+ * "Fix two synchronization gaps in the MiniMax M3 low-M split-K GEMM",
+ * Hardware verification); these are this library's own.
+ *   stage      LOWM_STAGE_LINE: W goes global -> LDS in whole 128-byte lines
  *              (8 rows x 128 B per direct-to-LDS load, non-temporal); each
  *              wavefront streams its own quarter of the K slice through a
  *              ring of `stages` slots of 16 rows x 64 K that only it reads,
- *              with no barrier in the main loop.  unroll must be 2; the K
- *              slice must be a multiple of 256 (K / split_k % 256 == 0),
- *              else the launch returns LOWM_ERR_UNSUPPORTED.
- *   rows       W rows (output columns) per workgroup tile: 16, 32 or 64.
- *   waves      wavefronts per workgroup: 4 for LDS, REG and LINE (the K slice of a
- *              rank is split between them and their sums are added in wave
- *              order), 1 for WAVE.
+ *              with no barrier in the main loop; activation operands go
+ *              straight into registers.  unroll must be 2; the K slice must
+ *              be a multiple of 256 (K / split_k % 256 == 0).  rows 16, or
+ *              32 with 2 stages; M <= 32.
+ *              LOWM_STAGE_PANEL: tiles of 64 rows, 16 per wavefront, each
+ *              wavefront walking the whole K slice; W as in LINE (a ring slot
+ *              per wavefront), the activation operand of each 64-K step
+ *              ("panel") loaded once per workgroup into an LDS ring of
+ *              `stages` steps that all wavefronts read, refilled only after a
+ *              workgroup barrier.  rows 64, unroll 2, stages 3, 4 or 6;
+ *              17 <= M <= 64; the K slice a multiple of 64.
+ *              LOWM_STAGE_LDS: W goes global -> an LDS ring of `stages`
+ *              stages shared by the workgroup; a stage holds 512 K of each of
+ *              the tile's rows, each direct-to-LDS load moving 1 KB of one
+ *              row; a stage is refilled only after a workgroup barrier that
+ *              every wavefront reaches once its reads of it are done.  unroll
+ *              must be 4; stages 2 or 3.
+ *              LOWM_STAGE_REG: W goes global -> registers, a ring of
+ *              `stages` register stages per wavefront, `unroll` 32-wide K
+ *              chunks (4, 8 or 16) per wavefront per stage; each wavefront
+ *              streams its own contiguous quarter of the K slice.  stages 2.
+ *   rows       W rows (output columns) per workgroup tile: 16 or 32 (LINE,
+ *              LDS, REG), 64 (PANEL).
+ *   waves      wavefronts per workgroup: always 4.
  *   unroll     see stage.
- *   stages     ring depth: 2, 3 or 4 (LDS), 2, 3 or 4 (REG), 2 or 4 (WAVE),
- *              2, 3 or 4 (LINE; rows 16, or 32 with 2 stages).
+ *   stages     ring depth, see stage.
+ * A tactic the build does not provide for the launch's M and K slice is
+ * LOWM_ERR_UNSUPPORTED.
  */
 #define LOWM_STAGE_LDS 0
 #define LOWM_STAGE_REG 1
-#define LOWM_STAGE_WAVE 2
 #define LOWM_STAGE_LINE 3
+#define LOWM_STAGE_PANEL 4
 typedef struct lowm_tactic {
     int stage;
     int rows;

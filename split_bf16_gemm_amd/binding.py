@@ -21,8 +21,8 @@ LOWM_ERR_WORKSPACE = -3
 LOWM_ERR_LAUNCH = -4
 LOWM_STAGE_LDS = 0
 LOWM_STAGE_REG = 1
-LOWM_STAGE_WAVE = 2
 LOWM_STAGE_LINE = 3
+LOWM_STAGE_PANEL = 4
 MAX_M = 64
 MAX_SPLIT_K = 256
 
@@ -42,17 +42,15 @@ class Tactic(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
     def __repr__(self) -> str:
-        st = {LOWM_STAGE_LDS: "lds", LOWM_STAGE_REG: "reg", LOWM_STAGE_WAVE: "wave",
-              LOWM_STAGE_LINE: "line"}.get(self.stage, str(self.stage))
+        st = {LOWM_STAGE_LDS: "lds", LOWM_STAGE_REG: "reg", LOWM_STAGE_LINE: "line",
+              LOWM_STAGE_PANEL: "panel"}.get(self.stage, str(self.stage))
         return (f"Tactic({st}, rows={self.rows}, waves={self.waves}, "
                 f"unroll={self.unroll}, stages={self.stages})")
 
 
-def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 0) -> Tactic:
-    code = {"lds": LOWM_STAGE_LDS, "reg": LOWM_STAGE_REG, "wave": LOWM_STAGE_WAVE,
-            "line": LOWM_STAGE_LINE}[stage]
-    if waves == 0:
-        waves = 1 if code == LOWM_STAGE_WAVE else 4
+def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 4) -> Tactic:
+    code = {"lds": LOWM_STAGE_LDS, "reg": LOWM_STAGE_REG, "line": LOWM_STAGE_LINE,
+            "panel": LOWM_STAGE_PANEL}[stage]
     return Tactic(code, rows, waves, unroll, stages)
 
 

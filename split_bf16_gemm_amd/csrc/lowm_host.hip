@@ -1,0 +1,527 @@
+// lowm_host.hip -- host side of the low-M split-K bf16 GEMM for AMD Instinct
+// MI355X (gfx950): argument validation, tactic and split_k choice, workspace
+// sizing, launch, the consumer-side wait of the push epilogue, and the C ABI
+// of include/lowm.h.  The kernels are in lowm_kernels.cuh, instantiated per
+// output kind in lowm_inst_*.hip.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lowm_types.h"
+
+namespace lowm {
+
+const Table& table() {
+  static const Table t = [] {
+    Table x{};
+    fill_table_bf16(x);
+    fill_table_f32(x);
+    fill_table_push(x);
+    return x;
+  }();
+  return t;
+}
+
+thread_local int g_last_hip_error = 0;
+StressArgs g_stress = {0u, -1, -1, 0, 0, -1, 0u, nullptr};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_sizes(int M, int N, int K, int S) {
+  if (M <= 0 || N <= 0 || K <= 0 || S < 1) return LOWM_ERR_INVALID_ARG;
+  if (M > LOWM_MAX_M || S > LOWM_MAX_SPLIT_K) return LOWM_ERR_UNSUPPORTED;
+  if (K % (kVecK * S) != 0) return LOWM_ERR_UNSUPPORTED;
+  return LOWM_OK;
+}
+
+size_t counter_bytes(int N) { return (size_t)4 * kCtrStride * ((N + 15) / 16); }
+// Every tile width 16*RG divides this, so tiles * BN <= round_up(N, kPartialPad).
+constexpr size_t kPartialPad = 64;
+
+int variant_index(const lowm_tactic& t) {
+  for (int i = 0; i < kNumVariants; ++i)
+    if (kVariants[i].stage == t.stage && kVariants[i].unroll == t.unroll &&
+        kVariants[i].stages == t.stages)
+      return i;
+  return -1;
+}
+
+int rows_index(int rows) { return rows % 16 == 0 ? rg_index(rows / 16) : -1; }
+
+KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t, bool push = false) {
+  if (t.waves != kWaves) return nullptr;
+  const int ri = rows_index(t.rows);
+  const int vi = variant_index(t);
+  if (ri < 0 || vi < 0 || M < 1 || M > LOWM_MAX_M) return nullptr;
+  return table().fn[push ? kOutPush : f32out ? kOutF32 : kOutBf16][act][(M + 15) / 16 - 1][ri][vi];
+}
+
+// Largest activation slice staged in LDS (bytes, padding included).
+constexpr size_t kActLdsMax = 48 * 1024;
+size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
+
+// Default tactic.  Where the K slice is whole 64-K line pairs per wavefront
+// (K / split_k % 256 == 0) and M <= 32: line-pair tiles of 16 rows, a ring of
+// 4 slots for M <= 4 with 8..15 pairs per wavefront and of 2 otherwise; not
+// for M > 16 with 16 or more pairs, where the register ring below is faster.
+// Measured on MI355X at N 6144, K 4096, M 1..32, split_k 1..8, and at
+// N 2304 K 12288 split_k 4 and N 49152 K 4096 split_k 2: the line tiles
+// beat the register ring by 3-30 % everywhere else.
+// Otherwise tiles of 16 weight rows for M <= 16 and 32 above (two row
+// groups share each activation load) in a register ring: each of the four
+// wavefronts streams cpw = ceil(chunks / 4) contiguous chunks of its slice.
+// When cpw <= 16 the best ring issues the whole range in its first stage
+// (unroll = the smallest power of two >= cpw, 2 stages); for longer ranges a
+// 4-chunk, 2-stage ring beats deeper ones.  Fall back to other rings, then
+// the LDS variants, when the build has no such instantiation for this M.
+int pick(int M, int N, int K, int S, lowm_tactic* t) {
+  const int rc = check_sizes(M, N, K, S);
+  if (rc != LOWM_OK) return rc;
+  const int nvec = K / S / kVecK;
+  const int cpw = ((nvec + 3) / 4 + kWaves - 1) / kWaves;
+  const int act = (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) ? 1 : 0;
+  int first_unroll = 4;
+  if (cpw <= 16) {
+    while (first_unroll < cpw) first_unroll *= 2;
+  }
+  const Variant first = {kStageReg, first_unroll, 2};
+  static const Variant others[] = {{kStageReg, 4, 2}, {kStageReg, 8, 2}, {kStageLds, 4, 2},
+                                   {kStageLds, 4, 3}};
+  t->rows = M <= 16 ? 16 : 32;
+  // The launch stages the activation slice in LDS when `act` is 1 and the
+  // build has that instantiation, else it loads activation operands from L2;
+  // the tactic must exist in the mode the launch will use.
+  auto provides = [&](const Variant& v) {
+    t->stage = v.stage;
+    t->unroll = v.unroll;
+    t->stages = v.stages;
+    t->waves = kWaves;
+    for (int f = 0; f < 2; ++f) {
+      const bool f32 = f == 1;
+      if (!(act && lookup(f32, 1, M, *t)) && !lookup(f32, 0, M, *t)) return false;
+    }
+    return true;
+  };
+  // More than 16 activation rows: panel tiles (the activation operand of a
+  // step shared in LDS by the four wavefronts), ring of 4 steps.  Measured on
+  // MI355X at M 32 and M 64, N 6144, K 4096, split_k 1..8: 1.3-2.1x faster
+  // than the line-pair and register tiles at every point; rings of 3 and 6
+  // are within a few percent, 3 slower at M 64.
+  if (M > 16 && nvec % 8 == 0) {
+    t->rows = 64;
+    if (provides({kStagePanel, 2, 4})) return LOWM_OK;
+  }
+  if (nvec % 32 == 0 && M <= 32) {
+    const int pairs = nvec / 32;   // line pairs per wavefront
+    // Measured on MI355X: 32-row line tiles beat 16-row ones only without
+    // split-K, for 5..16 activation rows, 16 line pairs per wavefront and at
+    // least 192 tiles (M 16, N 6144, K 4096: 12.3 vs 14.4 us; M 16, N 24576:
+    // 32.9 vs 40.5); with split_k 2..8, other slice lengths or fewer tiles
+    // they lose.
+    if (S == 1 && M > 4 && M <= 16 && pairs == 16 && (N + 31) / 32 >= 192) {
+      t->rows = 32;
+      if (provides({kStageLine, 2, 2})) return LOWM_OK;
+    }
+    if (!(M > 16 && pairs >= 16)) {
+      const int ring = (M <= 4 && pairs >= 8 && pairs < 16) ? 4 : 2;
+      t->rows = 16;
+      if (provides({kStageLine, 2, ring})) return LOWM_OK;
+    }
+  }
+  t->rows = M <= 16 ? 16 : 32;
+  if (provides(first)) return LOWM_OK;
+  for (const Variant& v : others)
+    if (provides(v)) return LOWM_OK;
+  return LOWM_ERR_UNSUPPORTED;
+}
+
+// split_k for a shape, from a table of the fastest measured on MI355X (default
+// tactic for each split_k, W streamed from HBM): M 4 and 16, N 768 .. 24576,
+// K 2048 .. 16384, split_k 1, 2, 4, 8.  A shape takes its nearest grid point
+// in log2 N and log2 K; M <= 8 uses the M 4 row, larger M the M 16 row.  On
+// the grid every entry is the fastest split_k; off it, the neighbours were
+// within 10 % of each other's best.  split_k pays when the tiles are few and
+// K is long; for M 16 the larger partials make it pay less often.
+constexpr unsigned char kBestSplit[2][6][4] = {
+    // M <= 8            K: 2048 4096 8192 16384
+    {{1, 4, 4, 8},    // N 768
+     {2, 2, 4, 4},    // N 1536
+     {1, 2, 2, 4},    // N 3072
+     {1, 2, 2, 8},    // N 6144
+     {1, 1, 2, 8},    // N 12288
+     {1, 1, 2, 8}},   // N 24576
+    // M > 8
+    {{1, 4, 4, 4},
+     {1, 2, 8, 8},
+     {1, 1, 4, 4},
+     {1, 1, 2, 4},
+     {1, 1, 1, 1},
+     {1, 1, 1, 1}}};
+
+int nearest_log2_index(double x, double base, int last) {
+  const int i = (int)floor(log2(x / base) + 0.5);
+  return i < 0 ? 0 : (i > last ? last : i);
+}
+
+int pick_split(int M, int N, int K, int* split_k) {
+  if (!split_k) return LOWM_ERR_INVALID_ARG;
+  int rc = check_sizes(M, N, K, 1);
+  if (rc != LOWM_OK) return rc;
+  int S = kBestSplit[M <= 8 ? 0 : 1][nearest_log2_index(N, 768.0, 5)]
+                    [nearest_log2_index(K, 2048.0, 3)];
+  // the largest power of two <= S that K allows (a whole number of 16-byte
+  // vectors per slice), preferring slices that are whole line pairs
+  while (S > 1 && K % (kVecK * S) != 0) S /= 2;
+  while (S > 1 && (K / S) % 256 != 0 && K % 256 == 0) S /= 2;
+  *split_k = S;
+  return LOWM_OK;
+}
+
+// The kernel a launch with tactic t runs: the activation slice is staged in
+// LDS when it is small and whole 1 KB pieces (and the build has that
+// instantiation); otherwise the wavefronts load activation operands from L2.
+KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_t* dyn_lds,
+                       bool push = false) {
+  *dyn_lds = 0;
+  // line-pair tiles stream whole 64-K line pairs per wavefront; panel tiles
+  // whole 64-K steps of the slice
+  if (t.stage == kStageLine && nvec % 32 != 0) return nullptr;
+  if (t.stage == kStagePanel && nvec % 8 != 0) return nullptr;
+  if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
+    if (KernelFn fn = lookup(f32out, 1, M, t, push)) {
+      *dyn_lds = act_lds_bytes(M, nvec);
+      return fn;
+    }
+  }
+  *dyn_lds = 0;
+  return lookup(f32out, 0, M, t, push);
+}
+
+size_t workspace_bytes(int M, int N, int K, int S) {
+  if (check_sizes(M, N, K, S) != LOWM_OK || S == 1) return 0;
+  // counters for up to ceil(N/16) tiles, then [tiles][split_k][M][BN] fp32
+  // partials; tiles * BN never exceeds N rounded up to 64, a multiple of
+  // every tile width.  Both parts are multiples of 256 bytes.
+  return counter_bytes(N) + (size_t)S * (size_t)M * round_up((size_t)N, kPartialPad) * sizeof(float);
+}
+
+// The push epilogue of a single-GEMM launch (bf16 output).
+struct PushSpec {
+  void* dst;
+  int ld;
+  uint32_t* flags;
+  uint32_t value;
+};
+
+// [lo, hi) of the bytes a row-major [rows, cols] array with row pitch ld
+// elements of `elem` bytes spans.
+inline void byte_span(const void* p, int rows, int cols, int ld, size_t elem, uintptr_t* lo,
+                      uintptr_t* hi) {
+  *lo = (uintptr_t)p;
+  *hi = *lo + ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * elem;
+}
+
+int check_push(const PushSpec& p, const void* C, int M, int N) {
+  if (!p.dst || !p.flags || p.value == 0 || p.ld < N) return LOWM_ERR_INVALID_ARG;
+  if (((uintptr_t)p.dst & 1) || ((uintptr_t)p.flags & 3)) return LOWM_ERR_UNSUPPORTED;
+  uintptr_t c0, c1, d0, d1, f0, f1;
+  byte_span(C, M, N, N, 2, &c0, &c1);
+  byte_span(p.dst, M, N, p.ld, 2, &d0, &d1);
+  byte_span(p.flags, 1, (N + 15) / 16, 0, 4, &f0, &f1);
+  auto overlap = [](uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+    return a0 < b1 && b0 < a1;
+  };
+  if (overlap(c0, c1, d0, d1) || overlap(c0, c1, f0, f1) || overlap(d0, d1, f0, f1))
+    return LOWM_ERR_INVALID_ARG;
+  return LOWM_OK;
+}
+
+// One launch of `count` GEMMs sharing M, K, split_k, the output type and the
+// tactic; the single-GEMM entry points are the count == 1 case.  GEMM g's
+// workspace follows GEMM g-1's (each is workspace_bytes of its own sizes).
+// `push` (single bf16 GEMM only) adds the push epilogue.
+int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int K, int S,
+                 void* workspace, hipStream_t stream, const lowm_tactic* tactic,
+                 const PushSpec* push = nullptr) {
+  if (!gemms || count < 1) return LOWM_ERR_INVALID_ARG;
+  if (count > kMaxBatch) return LOWM_ERR_UNSUPPORTED;
+  if (push && (count != 1 || f32out)) return LOWM_ERR_INVALID_ARG;
+  for (int g = 0; g < count; ++g)
+    if (!gemms[g].A || !gemms[g].W || !gemms[g].C) return LOWM_ERR_INVALID_ARG;
+  int rc = LOWM_OK;
+  for (int g = 0; g < count; ++g) {
+    rc = check_sizes(M, gemms[g].N, K, S);
+    if (rc != LOWM_OK) return rc;
+  }
+  if (S > 1 && !workspace) return LOWM_ERR_WORKSPACE;
+  for (int g = 0; g < count; ++g) {
+    if (((uintptr_t)gemms[g].A | (uintptr_t)gemms[g].W) & 15) return LOWM_ERR_UNSUPPORTED;
+    if ((uintptr_t)gemms[g].C & (f32out ? 3 : 1)) return LOWM_ERR_UNSUPPORTED;
+  }
+  if (S > 1 && ((uintptr_t)workspace & 15)) return LOWM_ERR_UNSUPPORTED;
+  if (push) {
+    rc = check_push(*push, gemms[0].C, M, gemms[0].N);
+    if (rc != LOWM_OK) return rc;
+  }
+
+  lowm_tactic t;
+  if (tactic) {
+    t = *tactic;
+  } else {
+    // One tactic serves every GEMM of the launch: pick it for the narrowest
+    // (the only rule that depends on N asks for enough tiles).
+    int n_min = gemms[0].N;
+    for (int g = 1; g < count; ++g) n_min = gemms[g].N < n_min ? gemms[g].N : n_min;
+    rc = pick(M, n_min, K, S, &t);
+    if (rc != LOWM_OK) return rc;
+  }
+  const int nvec = K / S / kVecK;
+  size_t dyn_lds = 0;
+  const KernelFn fn = select_kernel(f32out, M, nvec, t, &dyn_lds, push != nullptr);
+  if (!fn) return LOWM_ERR_UNSUPPORTED;
+
+  const int BN = t.rows;
+  Batch bt{};
+  size_t grid = 0, ws_off = 0;
+  for (int g = 0; g < count; ++g) {
+    GemmSlot& sl = bt.g[g];
+    const int N = gemms[g].N;
+    sl.A = static_cast<const uint16_t*>(gemms[g].A);
+    sl.W = static_cast<const uint16_t*>(gemms[g].W);
+    sl.C = gemms[g].C;
+    sl.N = N;
+    char* ws = static_cast<char*>(workspace) + ws_off;
+    sl.ctr = S > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+    sl.part = S > 1 ? reinterpret_cast<uint32_t*>(ws + counter_bytes(N)) : nullptr;
+    ws_off += workspace_bytes(M, N, K, S);
+    const size_t tiles = (size_t)((N + BN - 1) / BN);
+    grid += round_up(tiles, kXcds) * (size_t)S;
+    if (grid > 0x7fffffffu) return LOWM_ERR_UNSUPPORTED;
+    sl.bid_end = (int)grid;
+  }
+  for (int g = count; g < kMaxBatch; ++g) bt.g[g] = bt.g[count - 1];
+
+  Args a{};
+  a.A = bt.g[0].A;
+  a.W = bt.g[0].W;
+  a.C = bt.g[0].C;
+  a.M = M;
+  a.N = bt.g[0].N;
+  a.K = K;
+  a.S = S;
+  a.nvec = nvec;
+  a.batch = count;
+  a.ctr = bt.g[0].ctr;
+  a.part = bt.g[0].part;
+  a.bid_base = 0;
+  a.push = push ? static_cast<uint16_t*>(push->dst) : nullptr;
+  a.flags = push ? push->flags : nullptr;
+  a.push_ld = push ? push->ld : 0;
+  a.flag_value = push ? push->value : 0u;
+  a.stress = g_stress;
+
+  void* kargs[] = {&a, &bt};
+  hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
+                                   dim3(kThreads), kargs, dyn_lds, stream);
+  if (err == hipSuccess) err = hipGetLastError();
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return LOWM_ERR_LAUNCH;
+  }
+  return LOWM_OK;
+}
+
+int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int K, int S,
+           void* workspace, hipStream_t stream, const lowm_tactic* tactic,
+           const PushSpec* push = nullptr) {
+  const lowm_gemm_desc one = {A, W, C, N};
+  return launch_batch(&one, 1, f32out, M, K, S, workspace, stream, tactic, push);
+}
+
+// Consumer side of the push epilogue: one wavefront polls the flags with
+// system-scope loads until each holds `value` or `ticks` of the 100 MHz
+// real-time counter have passed, then writes how many flags it did not see
+// set (0: all were).  Every poll of a flag is a fresh load; a flag once seen
+// is not polled again.
+constexpr int kWaitFlagsPerLane = 64;
+constexpr int kMaxWaitFlags = kWave * kWaitFlagsPerLane;
+constexpr uint32_t kMaxWaitUs = 10u * 1000u * 1000u;
+
+__global__ __launch_bounds__(kWave) void lowm_push_wait_kernel(const uint32_t* flags, int n,
+                                                                uint32_t value, uint64_t ticks,
+                                                                int* missing) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x;
+  uint64_t pending = 0;   // bit j: flag lane + 64 j not yet seen
+  for (int j = 0; j < kWaitFlagsPerLane; ++j)
+    if (lane + kWave * j < n) pending |= 1ull << j;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    for (int j = 0; j < kWaitFlagsPerLane; ++j) {
+      if (!(pending >> j & 1)) continue;
+      const uint32_t f = __hip_atomic_load(flags + lane + kWave * j, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+      if (f == value) pending &= ~(1ull << j);
+    }
+    if (__all(pending == 0)) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  int left = __popcll(pending);
+  for (int off = kWave / 2; off > 0; off >>= 1) left += __shfl_xor(left, off);
+  if (lane == 0) missing[0] = left;
+#endif
+}
+
+int push_wait(const uint32_t* flags, int n, uint32_t value, uint32_t timeout_us, int* missing,
+              hipStream_t stream) {
+  if (!flags || !missing || n < 1 || value == 0) return LOWM_ERR_INVALID_ARG;
+  if (n > kMaxWaitFlags || timeout_us > kMaxWaitUs) return LOWM_ERR_UNSUPPORTED;
+  if (((uintptr_t)flags & 3) || ((uintptr_t)missing & 3)) return LOWM_ERR_UNSUPPORTED;
+  const uint64_t ticks = (uint64_t)timeout_us * 100u;
+  void* kargs[] = {&flags, &n, &value, const_cast<uint64_t*>(&ticks), &missing};
+  hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&lowm_push_wait_kernel),
+                                   dim3(1), dim3(kWave), kargs, 0, stream);
+  if (err == hipSuccess) err = hipGetLastError();
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return LOWM_ERR_LAUNCH;
+  }
+  return LOWM_OK;
+}
+
+}  // namespace lowm
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int lowm_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int split_k,
+                     void* workspace, void* stream) {
+  return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
+                      static_cast<hipStream_t>(stream), nullptr);
+}
+
+int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C, int M, int N, int K,
+                            int split_k, void* workspace, void* stream) {
+  return lowm::launch(A, W, C, true, M, N, K, split_k, workspace,
+                      static_cast<hipStream_t>(stream), nullptr);
+}
+
+int lowm_gemm_splitk_ex(const void* A, const void* W, void* C, int M, int N, int K,
+                        int split_k, void* workspace, void* stream, const lowm_tactic* tactic) {
+  return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
+                      static_cast<hipStream_t>(stream), tactic);
+}
+
+int lowm_gemm_splitk_f32out_ex(const void* A, const void* W, float* C, int M, int N, int K,
+                               int split_k, void* workspace, void* stream,
+                               const lowm_tactic* tactic) {
+  return lowm::launch(A, W, C, true, M, N, K, split_k, workspace,
+                      static_cast<hipStream_t>(stream), tactic);
+}
+
+size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k) {
+  return lowm::workspace_bytes(M, N, K, split_k);
+}
+
+int lowm_gemm_splitk_push(const void* A, const void* W, void* C, int M, int N, int K,
+                          int split_k, void* workspace, void* push, int push_ld,
+                          uint32_t* flags, uint32_t flag_value, void* stream,
+                          const lowm_tactic* tactic) {
+  const lowm::PushSpec ps = {push, push_ld, flags, flag_value};
+  return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
+                      static_cast<hipStream_t>(stream), tactic, &ps);
+}
+
+int lowm_push_wait(const uint32_t* flags, int n_flags, uint32_t flag_value,
+                   uint32_t timeout_us, int* missing, void* stream) {
+  return lowm::push_wait(flags, n_flags, flag_value, timeout_us, missing,
+                         static_cast<hipStream_t>(stream));
+}
+
+int lowm_gemm_splitk_batched(const lowm_gemm_desc* gemms, int count, int M, int K,
+                             int split_k, void* workspace, void* stream) {
+  return lowm::launch_batch(gemms, count, false, M, K, split_k, workspace,
+                            static_cast<hipStream_t>(stream), nullptr);
+}
+
+size_t lowm_gemm_splitk_batched_workspace_bytes(const lowm_gemm_desc* gemms, int count, int M,
+                                                int K, int split_k) {
+  if (!gemms || count < 1 || count > LOWM_MAX_BATCH) return 0;
+  size_t total = 0;
+  for (int g = 0; g < count; ++g) {
+    if (lowm::check_sizes(M, gemms[g].N, K, split_k) != LOWM_OK) return 0;
+    total += lowm::workspace_bytes(M, gemms[g].N, K, split_k);
+  }
+  return total;
+}
+
+int lowm_pick_split_k(int M, int N, int K, int* split_k) {
+  return lowm::pick_split(M, N, K, split_k);
+}
+
+int lowm_check_launch(int M, int N, int K, int split_k, int f32out, const lowm_tactic* tactic) {
+  int rc = lowm::check_sizes(M, N, K, split_k);
+  if (rc != LOWM_OK) return rc;
+  lowm_tactic t;
+  if (tactic) {
+    t = *tactic;
+  } else {
+    rc = lowm::pick(M, N, K, split_k, &t);
+    if (rc != LOWM_OK) return rc;
+  }
+  size_t dyn = 0;
+  return lowm::select_kernel(f32out != 0, M, K / split_k / lowm::kVecK, t, &dyn)
+             ? LOWM_OK
+             : LOWM_ERR_UNSUPPORTED;
+}
+
+int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out) {
+  if (!out) return LOWM_ERR_INVALID_ARG;
+  return lowm::pick(M, N, K, split_k, out);
+}
+
+const char* lowm_strerror(int code) {
+  switch (code) {
+    case LOWM_OK: return "success";
+    case LOWM_ERR_INVALID_ARG: return "invalid argument (NULL operand, size <= 0, split_k < 1)";
+    case LOWM_ERR_UNSUPPORTED:
+      return "unsupported (M > 64, K not a multiple of 8*split_k, split_k > 256, misaligned "
+             "pointer, or tactic not in this build)";
+    case LOWM_ERR_WORKSPACE: return "split_k > 1 needs a workspace";
+    case LOWM_ERR_LAUNCH: return "kernel launch failed (see lowm_last_hip_error)";
+    default: return "unknown error code";
+  }
+}
+
+int lowm_last_hip_error(void) { return lowm::g_last_hip_error; }
+
+#ifdef LOWM_STRESS
+// Stress build only: where, on whom and how long the kernels stall.  Applies
+// to every later launch from any thread; not thread-safe.
+int lowm_stress_configure(unsigned site_mask, int rank, int wave, int tile_mod, int tile_sel,
+                          int step, unsigned delay_ns) {
+  if (delay_ns > 1000000u) return LOWM_ERR_INVALID_ARG;  // at most 1 ms per stall
+  lowm::g_stress.site_mask = site_mask;
+  lowm::g_stress.rank = rank;
+  lowm::g_stress.wave = wave;
+  lowm::g_stress.tile_mod = tile_mod;
+  lowm::g_stress.tile_sel = tile_sel;
+  lowm::g_stress.step = step;
+  lowm::g_stress.ticks = delay_ns / 10u;  // s_memrealtime: 100 MHz
+  return LOWM_OK;
+}
+
+// Stress build only: record per-workgroup timestamps into `buf` (device
+// memory, 8 uint64 per workgroup of the grid; NULL stops tracing).
+int lowm_stress_trace(void* buf) {
+  lowm::g_stress.trace = static_cast<uint64_t*>(buf);
+  return LOWM_OK;
+}
+#endif
+
+}  // extern "C"

@@ -1,4 +1,8 @@
-// lowm_splitk.hip -- low-M split-K bf16 GEMM for AMD Instinct MI355X (gfx950).
+// lowm_kernels.cuh -- device code of the low-M split-K bf16 GEMM for AMD
+// Instinct MI355X (gfx950): helpers, the split-K exchange, and the kernel
+// templates.  Included by the per-output-kind translation units
+// (lowm_inst_*.hip), each of which instantiates its kernels and fills its
+// part of the kernel table.
 //
 //   C[m][n] = sum_k A[m][k] * W[n][k]        A [M,K], W [N,K] bf16, row-major
 //
@@ -8,46 +12,52 @@
 // K cut into split_k slices whose fp32 partials one owner adds.  The design
 // here is gfx950's own:
 //
-//  * One workgroup = (output tile of BN = 16*RG weight rows) x (one K slice,
-//    "rank").  Its four wavefronts share the slice; each streams its share of
-//    W once from HBM and feeds bf16 MFMA 16x16x32 with W as the 16-column
-//    operand and the M activation rows, zero-padded to 16 per block, as the
-//    16-row operand, accumulating fp32 in registers.  M <= 64 is 1..4 MFMA
-//    row blocks.
-//  * W reaches the MFMA either through an LDS ring of NS stages filled with
-//    direct-to-LDS loads (global_load_lds_dwordx4) and shared by the whole
-//    workgroup, or straight into a ring of NS register stages per wavefront.
-//    In the LDS ring a stage is refilled only after a workgroup barrier that
-//    every wavefront reaches once its reads of that stage have completed: a
-//    per-wavefront wait is not enough when the stage is shared (Triton issue
-//    "warpgroup_mma_wait does not properly synchronize across warpgroups";
-//    cuLA PR "Fix SM90 WY input buffer reuse before WGMMA completion").
-//  * The wavefronts' sums are added through LDS in wavefront order.
-//  * split_k > 1: every rank stores its fp32 partial in the workspace, makes
-//    it visible at agent scope (release), and counts itself in the tile's
-//    arrival counter with a relaxed atomic.  The rank that sees split_k-1
-//    earlier arrivals is the owner: it reads the peers' partials after the
-//    count (acquire), adds the partials in rank order 0..split_k-1 (its own
-//    from registers, at its own position), rounds once to bf16 and returns
-//    the counter and the tile's partial slots to zero.  A slot word holds the
-//    complement of the partial's bits, so zero means "not published"; the
-//    whole workspace is zero between launches.  Where split_k is 2..4 and a
-//    tile has at most 64 elements, the grid is rank-major and the tile's last
-//    rank polls its peers' slots for a bounded time instead of publishing: a
-//    published slot is visible long before the publisher's acknowledgement
-//    and arrival come back from the loaded memory system.  Each counter sits
-//    on its own 256-byte line: device-scope atomics on one line are
-//    serialised where they execute, so tiles do not share lines.  Scope
-//    matters (PR, Description item 2: a release and an acquire synchronize
-//    only when each one's scope includes the other thread); the acquire is
-//    carried by device-scope loads issued on the owner's path only (PR,
-//    Description item 2, on the cost of an acquiring wait).  No workgroup
-//    waits for another without a bound.
+//  * One workgroup = (output tile of BN weight rows) x (one K slice, "rank").
+//    Its four wavefronts stream W once from HBM and feed bf16 MFMA 16x16x32
+//    with W as the 16-column operand and the M activation rows, in blocks of
+//    16, as the 16-row operand, accumulating fp32 in registers.  M <= 64 is
+//    1..4 MFMA row blocks.
+//  * Tile kinds (tactics):
+//      LINE   W global -> LDS in whole 128-byte lines (non-temporal
+//             direct-to-LDS loads) into a ring private to each wavefront;
+//             the wavefronts split the K slice; activation operands straight
+//             from memory into registers.  The default for M <= 16.
+//      PANEL  64-row tiles, each wavefront owning 16 of them for the whole K
+//             slice; W as in LINE, and the activation panel of each 64-K
+//             step loaded once per workgroup into an LDS ring that all four
+//             wavefronts read, refilled only after a workgroup barrier.
+//             Each wavefront then owns its 16 output columns through the
+//             exchange as well.  The default for M > 16.
+//      REG    W global -> a register ring per wavefront (any K slice).
+//      LDS    W global -> an LDS ring of NS stages shared by the workgroup,
+//             a stage refilled only after a workgroup barrier that every
+//             wavefront reaches once its reads of it have completed: a
+//             per-wavefront wait is not enough when the stage is shared
+//             (Triton issue "warpgroup_mma_wait does not properly
+//             synchronize across warpgroups"; cuLA PR "Fix SM90 WY input
+//             buffer reuse before WGMMA completion").
+//  * split_k > 1: every rank stores its fp32 partial in the workspace slots
+//    and counts itself in the arrival counter of its columns with a relaxed
+//    device-scope atomic.  The rank that sees split_k-1 earlier arrivals is
+//    the owner: it reads the peers' slots, adds the partials in rank order
+//    0..split_k-1 (its own from registers, at its own position), rounds once
+//    to bf16 and returns the counter and the slots to zero.  A slot word
+//    holds the complement of the partial's bits, so zero means "not
+//    published": each slot is its own single-copy-atomic object, written
+//    once per launch, and the owner re-reads any slot it still finds zero
+//    (bounded) instead of relying on an ordering between the counter and the
+//    slots.  Where split_k is 2..4 and a tile has at most 64 elements, the
+//    grid is rank-major and the tile's last rank polls its peers' slots for a
+//    bounded time instead of publishing.  Scope matters (PR, Description
+//    item 2: a release and an acquire synchronize only when each one's scope
+//    includes the other thread): every exchanged access is at device
+//    ("agent") scope, the one that spans all XCDs.  No workgroup waits for
+//    another without a bound.
 //
-// Built twice from this source: liblowm.so, and liblowm_stress.so with
-// -DLOWM_STRESS, which adds bounded s_sleep stalls at chosen sites, ranks,
-// wavefronts and tiles (the stall-injection method of the PR's Hardware
-// verification).
+// Built twice: liblowm.so, and liblowm_stress.so with -DLOWM_STRESS, which
+// adds bounded s_sleep stalls at chosen sites, ranks, wavefronts and tiles
+// (the stall-injection method of the PR's Hardware verification).
+#pragma once
 
 #include <hip/hip_runtime.h>
 
@@ -58,100 +68,13 @@
 #include <type_traits>
 #include <utility>
 
-#include "lowm.h"
+#include "lowm_types.h"
 
 namespace lowm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWave = 64;        // lanes per wavefront
-constexpr int kWaves = 4;        // wavefronts per workgroup
-constexpr int kThreads = kWaves * kWave;
-constexpr int kVecK = 8;         // bf16 per 16-byte vector
-constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kCtrStride = 64;   // uint32 words between tile counters (256 bytes)
-constexpr int kProbeRanks = 3;   // early probe: at most 3 peers (split_k <= 4)
-constexpr uint32_t kProbeTicks = 2000;  // ... polled for at most 20 us (100 MHz clock)
-
-enum Stage : int {
-  kStageLds = LOWM_STAGE_LDS,
-  kStageReg = LOWM_STAGE_REG,
-  kStageWave = LOWM_STAGE_WAVE,
-  kStageLine = LOWM_STAGE_LINE
-};
-
-// ---------------------------------------------------------------------------
-// Stress instrumentation (compiled only with -DLOWM_STRESS)
-// ---------------------------------------------------------------------------
-enum StressSite : uint32_t {
-  kSiteEntry = 1u,        // a wavefront stalls before its first load
-  kSiteStageRead = 2u,    // after the stage barrier, before reading the stage
-  kSiteReduce = 4u,       // before writing its sums for the wavefront reduction
-  kSitePublish = 8u,      // before storing the rank partial and arriving
-  kSiteFold = 16u,        // owner: after the acquire, before reading partials
-};
-
-struct StressArgs {
-  uint32_t site_mask;     // OR of StressSite
-  int rank;               // -1: any rank
-  int wave;               // -1: any wavefront
-  int tile_mod;           // stall tiles with tile % tile_mod == tile_sel
-  int tile_sel;
-  int step;               // kSiteStageRead: only this step (-1: every step)
-  uint32_t ticks;         // stall length in s_memrealtime ticks (100 MHz)
-  uint64_t* trace;        // optional per-workgroup timestamps (kTraceSlots each)
-};
-
-// Timestamp trace of the stress build: per workgroup, s_memrealtime (100 MHz)
-// at these points, then the hardware ids of the CU and XCD it ran on.  The
-// timestamps are global stores, counted by the same vector-memory counter as
-// the loads whose completion the explicit s_waitcnt of the LDS-ring variants
-// assumes: a traced launch measures timing only, its output is not checked.
-enum TraceSlot : int {
-  kTraceEntry = 0, kTraceFirstStage = 1, kTraceLoopEnd = 2, kTraceReduced = 3,
-  kTraceArrived = 4, kTraceEnd = 5, kTraceHwId = 6, kTraceXccId = 7, kTraceSlots = 8
-};
-
-struct Args {
-  // Every field a single-GEMM launch reads sits in the first 64 bytes of the
-  // argument segment, so each workgroup's start waits for one scalar line.
-  const uint16_t* A;
-  const uint16_t* W;
-  void* C;
-  uint32_t* ctr;          // [tiles] arrival counters, kCtrStride words apart
-  uint32_t* part;         // [tiles][S][M*BN] encoded fp32 partials
-  int M, N, K, S;
-  int nvec;               // 16-byte vectors per rank slice: K / S / 8
-  int batch;              // GEMMs in the launch; 1: these fields describe the only one
-  // Set by gemm_args in the kernel, never read from the argument segment.
-  int bid_base;           // first workgroup of this GEMM in a batched launch
-  // push epilogue (its own instantiation, bf16 output)
-  uint16_t* push;         // exchange buffer, element (m, n) at push[m * push_ld + n]
-  uint32_t* flags;        // [ceil(N / 16)] one per 16 output columns
-  int push_ld;
-  uint32_t flag_value;
-  StressArgs stress;
-};
-static_assert(offsetof(Args, batch) + sizeof(int) <= 64, "hot fields leave the first line");
-
-// Batched launch: up to kMaxBatch independent GEMMs with one M, K and split_k
-// in one grid.  GEMM g owns the workgroups [bid_end of g-1, bid_end of g),
-// each range a multiple of 8 so that the ranks of a tile still share an XCD.
-constexpr int kMaxBatch = LOWM_MAX_BATCH;
-struct GemmSlot {
-  const uint16_t* A;
-  const uint16_t* W;
-  void* C;
-  uint32_t* ctr;
-  uint32_t* part;
-  int N;
-  int bid_end;
-};
-struct Batch {
-  GemmSlot g[kMaxBatch];  // read only when Args::batch > 1
-};
 
 // The Args of the GEMM this workgroup belongs to.
 __device__ __forceinline__ Args gemm_args(const Args& a, const Batch& bt) {
@@ -254,8 +177,8 @@ __device__ __forceinline__ u32x4 lds_read_opaque(const u32x4* p) {
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
   return v;
 }
-// 24 wait states after the last MFMA that writes any of `acc` (2 or 4
-// accumulators), before anything reads them.  Reading an MFMA result needs
+// 24 wait states after the last MFMA that writes any of `acc`, before
+// anything reads them.  Reading an MFMA result needs
 // wait states that the compiler inserts itself, but it was seen to omit them
 // on a path that branches from the last MFMA straight to the accumulator
 // reads (the first register then held its value from before the last two
@@ -266,10 +189,16 @@ __device__ __forceinline__ void mfma_settle(f32x4 (&acc)[N]) {
   if constexpr (N == 1) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]));
   else if constexpr (N == 2)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]));
+  else if constexpr (N == 3)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]));
   else if constexpr (N == 4)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                  : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
-  else static_assert(N == 1 || N == 2 || N == 4, "mfma_settle: 1, 2 or 4 accumulators");
+  else {
+    // in groups of four: each group's no-ops follow the MFMAs that write it
+    mfma_settle(reinterpret_cast<f32x4(&)[4]>(acc[0]));
+    mfma_settle(reinterpret_cast<f32x4(&)[N - 4]>(acc[4]));
+  }
 }
 
 // Waits for every outstanding LDS operation; the values read by
@@ -282,7 +211,13 @@ __device__ __forceinline__ void lds_wait(u32x4 (&v)[N]) {
   else if constexpr (N == 4)
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])
                  : : "memory");
-  else static_assert(N == 1 || N == 2 || N == 4, "lds_wait: 1, 2 or 4 values");
+  else {
+    // any count: the wait, then an empty asm per value that the value's uses
+    // depend on (volatile asm statements keep their order)
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+  }
 }
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -334,43 +269,108 @@ __device__ __forceinline__ void store_slot(uint32_t* p, uint32_t w) {
   __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The owner's value of one output element: the S rank partials of this tile
-// (slot r at slots[r * E + e]) added in rank order 0..S-1, with this rank's
-// own partial `own` at its own position.  The S-1 peers' slots are loaded
-// unconditionally (peer i is rank i, or i+1 past the owner) and before the
-// first add, so the loads overlap; a load under a branch would be waited for
-// inside it.  Loads only: the caller stores C and clears the slots after all
-// its folds, so that no wait for these loads also waits for stores.
-template <int SN>
-__device__ __forceinline__ float fold_ranks_n(const uint32_t* slots, size_t E, int e, int rank,
-                                              float own) {
-  uint32_t w[SN - 1];
-#pragma unroll
-  for (int i = 0; i < SN - 1; ++i)
-    w[i] = load_slot(slots + (size_t)(i < rank ? i : i + 1) * E + e);
-  float v = (rank == 0) ? own : dec_partial(w[0]);
-#pragma unroll
-  for (int r = 1; r < SN; ++r)
-    v += (r == rank) ? own : dec_partial(r < rank ? w[r < SN - 1 ? r : 0] : w[r - 1]);
-  return v;
+// The owner's fold.  For each of its NE elements e[j] (slot r of element e
+// at slots[r * E + e]) the S rank partials are added in rank order
+// 0..S-1, with this rank's own partial (v[j] on entry) at its own position;
+// v[j] holds the sum on exit.  The peers' slots (peer i is rank i, or i+1
+// past the owner) are all loaded before the first add, so the loads overlap;
+// a load under a branch would be waited for inside it.  Loads only: the
+// caller stores C and clears the slots after its folds, so that no wait for
+// these loads also waits for stores.
+//
+// The arrival counter only says when to look.  What the owner adds is what
+// each slot holds, and a slot is its own single-copy-atomic 32-bit object
+// that is zero until its rank writes it, once, in this launch.  So any
+// non-zero word read is that rank's partial, whatever order the memory
+// system made the counter and the slots visible in.  A word still zero is
+// re-read, with s_sleep between reads, for at most kFoldPollTicks of the
+// 100 MHz clock; one that stays zero is added as it is (it decodes as a NaN,
+// so C shows it) and the tile's fault word is set for the host to find.
+__device__ __forceinline__ const uint32_t* peer_slot(const uint32_t* slots, size_t E, int e,
+                                                     int rank, int i) {
+  return slots + (size_t)(i < rank ? i : i + 1) * E + e;
 }
 
-__device__ __forceinline__ float fold_ranks(const uint32_t* slots, size_t E, int e, int S,
-                                            int rank, float own) {
+template <int NW>
+__device__ __forceinline__ void await_published(uint32_t (&w)[NW], const uint32_t* const (&src)[NW],
+                                             uint32_t* fault) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  bool zero = true;
+  while (true) {
+    __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      if (w[i] == 0u) w[i] = __hip_atomic_load(src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    zero = false;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) zero = zero || w[i] == 0u;
+    if (!__any(zero)) return;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kFoldPollTicks) break;
+  }
+  if (zero) __hip_atomic_store(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int SN, int NE>
+__device__ __forceinline__ void fold_owner_n(const uint32_t* slots, size_t E, const int (&e)[NE],
+                                             int rank, float (&v)[NE], uint32_t* fault) {
+  constexpr int NW = NE * (SN - 1);
+  uint32_t w[NW];
+  const uint32_t* src[NW];
+#pragma unroll
+  for (int j = 0; j < NE; ++j)
+#pragma unroll
+    for (int i = 0; i < SN - 1; ++i) {
+      src[j * (SN - 1) + i] = peer_slot(slots, E, e[j], rank, i);
+      w[j * (SN - 1) + i] = load_slot(src[j * (SN - 1) + i]);
+    }
+  bool zero = false;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) zero = zero || w[i] == 0u;
+  if (__builtin_expect(__any(zero), 0)) await_published(w, src, fault);
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    const uint32_t* wj = w + j * (SN - 1);
+    float acc = (rank == 0) ? v[j] : dec_partial(wj[0]);
+#pragma unroll
+    for (int r = 1; r < SN; ++r)
+      acc += (r == rank) ? v[j] : dec_partial(r < rank ? wj[r < SN - 1 ? r : 0] : wj[r - 1]);
+    v[j] = acc;
+  }
+}
+
+// Any other split_k: one element and one peer at a time (a slow path; the
+// measured split_k choices are 2, 3, 4 and 8).
+template <int NE>
+__device__ __forceinline__ void fold_owner_any(const uint32_t* slots, size_t E,
+                                               const int (&e)[NE], int S, int rank,
+                                               float (&v)[NE], uint32_t* fault) {
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    float acc = 0.f;
+    for (int r = 0; r < S; ++r) {
+      float p = v[j];
+      if (r != rank) {
+        uint32_t w[1] = {load_slot(slots + (size_t)r * E + e[j])};
+        const uint32_t* src[1] = {slots + (size_t)r * E + e[j]};
+        if (__any(w[0] == 0u)) await_published(w, src, fault);
+        p = dec_partial(w[0]);
+      }
+      acc = (r == 0) ? p : acc + p;
+    }
+    v[j] = acc;
+  }
+}
+
+template <int NE>
+__device__ __forceinline__ void fold_owner(const uint32_t* slots, size_t E, const int (&e)[NE],
+                                           int S, int rank, float (&v)[NE], uint32_t* fault) {
   switch (S) {
-    case 2: return fold_ranks_n<2>(slots, E, e, rank, own);
-    case 3: return fold_ranks_n<3>(slots, E, e, rank, own);
-    case 4: return fold_ranks_n<4>(slots, E, e, rank, own);
-    case 8: return fold_ranks_n<8>(slots, E, e, rank, own);
-    default: break;
+    case 2: fold_owner_n<2>(slots, E, e, rank, v, fault); break;
+    case 3: fold_owner_n<3>(slots, E, e, rank, v, fault); break;
+    case 4: fold_owner_n<4>(slots, E, e, rank, v, fault); break;
+    case 8: fold_owner_n<8>(slots, E, e, rank, v, fault); break;
+    default: fold_owner_any(slots, E, e, S, rank, v, fault); break;
   }
-  float v = 0.f;
-  for (int r = 0; r < S; ++r) {
-    const uint32_t w = load_slot(slots + (size_t)r * E + e);
-    const float p = (r == rank) ? own : dec_partial(w);
-    v = (r == 0) ? p : v + p;
-  }
-  return v;
 }
 
 // Every rank's slot of element e back to zero, once the owner has read them
@@ -447,6 +447,25 @@ struct Shape {
       lds_bytes <= 128 * 1024 && stage_vgprs <= 224 && NS >= 2 && NS <= 4 &&
       (STAGE == kStageReg || U == 4) && (NS - 1) * group_loads <= 63 && (!ACT || MB <= 2);
 };
+
+// Wait until at most min(younger, YMAX) groups of N vector-memory operations
+// issued after the oldest outstanding group are still in flight (younger < 0
+// counts as 0).
+template <int N, int YMAX>
+__device__ __forceinline__ void wait_younger(int younger) {
+  static_assert(YMAX >= 0 && YMAX <= 7 && YMAX * N <= 63, "vmcnt is 6 bits");
+  younger = younger < YMAX ? younger : YMAX;
+  switch (younger) {
+    case 7: if constexpr (YMAX >= 7) { wait_vmcnt<7 * N>(); break; } [[fallthrough]];
+    case 6: if constexpr (YMAX >= 6) { wait_vmcnt<6 * N>(); break; } [[fallthrough]];
+    case 5: if constexpr (YMAX >= 5) { wait_vmcnt<5 * N>(); break; } [[fallthrough]];
+    case 4: if constexpr (YMAX >= 4) { wait_vmcnt<4 * N>(); break; } [[fallthrough]];
+    case 3: if constexpr (YMAX >= 3) { wait_vmcnt<3 * N>(); break; } [[fallthrough]];
+    case 2: if constexpr (YMAX >= 2) { wait_vmcnt<2 * N>(); break; } [[fallthrough]];
+    case 1: if constexpr (YMAX >= 1) { wait_vmcnt<N>(); break; } [[fallthrough]];
+    default: wait_vmcnt<0>(); break;
+  }
+}
 
 template <int N>
 __device__ __forceinline__ void wait_groups(int younger) {
@@ -617,9 +636,10 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
 
   // a4: publish this rank's partial, then arrive.  The partial is written
   // with device-scope stores (sc1: written through this XCD's L2 to where
-  // every XCD sees it) and the arrival is issued only after all of them are
-  // acknowledged (vmcnt(0)): the release is carried by the stores' own
-  // scope, so no cache-wide write-back is needed.
+  // every XCD reads) and the arrival is issued only after all of them are
+  // acknowledged (vmcnt(0)), so by the time the owner counts this arrival
+  // the slots are normally readable; the owner's fold does not depend on
+  // it (a slot it still finds zero is re-read).
   for (int e = lane; e < E; e += kWave) store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
   wait_vmcnt0();
   pin_issue();
@@ -633,27 +653,29 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
     return;
   }
 
-  // a5: the owner.  The peers' partials are read with device-scope loads
-  // (sc1), issued only after the arrival count is known, so they observe
-  // every partial whose arrival was counted; no cache-wide invalidate.  The
-  // fold is in rank order with this rank's partial, from LDS, at its own
-  // position; every slot read goes back to zero.
+  // a5: the owner.  The peers' partials are read with device-scope loads;
+  // a slot still zero is re-read (fold_owner).  The fold is in rank order
+  // with this rank's partial, from LDS, at its own position; every slot read
+  // goes back to zero.
   LOWM_STALL(kSiteFold, 0);
   // Two passes: the folds (global loads only, four elements' loads in
   // flight at once; each result replaces the element's wavefront-0 sum in
   // LDS, which nothing else reads), then the stores of C and the clearing
   // of the slots, which nothing waits for.  Past the tile's end a lane folds
   // its first element again and keeps nothing.
+  uint32_t* fault = ctr + kFaultWord;
   auto fold_pass = [&](auto sn_c) {
     constexpr int SN = decltype(sn_c)::value;
     for (int e0 = lane; e0 < E; e0 += 4 * kWave) {
+      int e[4];
       float v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kWave < E ? e0 + u * kWave : e0;
-        v[u] = SN > 0 ? fold_ranks_n<(SN > 0 ? SN : 2)>(slots, E, e, rank, rank_sum(e))
-                      : fold_ranks(slots, E, e, a.S, rank, rank_sum(e));
+        e[u] = e0 + u * kWave < E ? e0 + u * kWave : e0;
+        v[u] = rank_sum(e[u]);
       }
+      if constexpr (SN > 0) fold_owner_n<SN>(slots, E, e, rank, v, fault);
+      else fold_owner_any(slots, E, e, a.S, rank, v, fault);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (e0 + u * kWave < E) red_pos(e0 + u * kWave) = v[u];
@@ -1239,30 +1261,70 @@ __global__ __launch_bounds__(kThreads) void lowm_line_kernel(Args a0, Batch bt) 
 #endif
 }
 
+
 // ---------------------------------------------------------------------------
-// Wavefront tiles: one wavefront is the whole workgroup and owns a tile of
-// BN = 16*RG weight rows for its entire K slice, so no wavefront waits for
-// another: no LDS stage barrier and no wavefront reduction.  W streams into a
-// ring of NS register stages of U 32-wide chunks (16 B per lane per chunk and
-// row group); the ring is issued unconditionally (past the end of the slice
-// the addresses repeat the slice's last vector and the products are masked),
-// so the loop body has no branches and the compiler's wait counts stay exact.
+// Panel tiles (M > 16): a workgroup's tile is 64 weight rows, 16 per
+// wavefront, and every wavefront walks the rank's whole K slice in steps of
+// 64 K.  With 17..64 activation rows the activation operand of a step
+// (16*MB rows x 64 K) outweighs the weight operand of one wavefront (16 rows
+// x 64 K), so it is loaded once per workgroup, as 2*MB whole-line pieces of
+// 8 rows x 128 B spread over the wavefronts, into an LDS ring that all four
+// wavefronts read (the activation "panel").  The weight rows stream as in
+// the line-pair tiles: whole-line non-temporal direct-to-LDS loads into a
+// slot only this wavefront reads.  Ring slot s holds step p = s (mod R) of
+// both.  (Measured on MI355X and not adopted: the weights straight into a
+// register ring in the MFMA operand layout, and 32 columns per wavefront;
+// both were slower at every M 32 / M 64 sweep shape.)
+//
+// Step p: each wavefront waits for its own loads of step p (vmcnt), then a
+// workgroup barrier makes every wavefront's panel pieces of step p visible
+// to all and guarantees that every wavefront has completed its reads of
+// step p-1 (each waits for its LDS reads before it multiplies), so the slot
+// step p-1 used is refilled with step p+R-1 right after the barrier.  A
+// stage is never refilled before all of its readers are done (the lesson of
+// the Triton issue "warpgroup_mma_wait does not properly synchronize across
+// warpgroups" and of the cuLA PR "Fix SM90 WY input buffer reuse before
+// WGMMA completion").  No load is issued past the end of the slice, so the
+// ring drains in the last R-2 steps and no load is in flight at the end.
+//
+// Each wavefront owns its 16 output columns to the end: no wavefront
+// reduction, and with split_k > 1 it publishes, arrives and (as the owner)
+// folds its 16-column strip, with the counter of that strip.
 // ---------------------------------------------------------------------------
-template <int MB, int RG, int U, int NS, int ACT>
-struct WaveShape {
-  static constexpr int BN = 16 * RG;
-  static constexpr int stage_vgprs = NS * U * 4 * (RG + (ACT ? 0 : MB));
-  static constexpr bool valid = NS >= 2 && NS <= 4 && stage_vgprs <= 256 && (!ACT || MB <= 2);
+template <int MB, int R>
+struct PanelShape {
+  static constexpr int BN = 16 * kWaves;               // 64 weight rows, 16 per wavefront
+  static constexpr int kPP = 68;                        // u32x4 per 8-row piece (1088 B)
+  static constexpr int w_slot = 2 * kPP;                // one wavefront's weight step
+  static constexpr int a_slot = 2 * MB * kPP;           // the activation panel of a step
+  static constexpr int slot_elems = kWaves * w_slot + a_slot;
+  static constexpr int a_loads = (2 * MB + kWaves - 1) / kWaves;   // panel pieces per wavefront
+  static constexpr int step_loads = 2 + a_loads;        // vector-memory ops per step per wavefront
+  static constexpr int lds_bytes = R * slot_elems * 16;
+  static constexpr bool valid = MB >= 2 && MB <= 4 && R >= 3 && R <= 8 &&
+                                (R - 1) * step_loads <= 63 && lds_bytes <= 128 * 1024;
 };
 
-template <int MB, int RG, int U, int NS, int ACT, typename OutT>
-__device__ __forceinline__ void wave_tile_body(const Args& a) {
-  constexpr int BN = 16 * RG;
-  extern __shared__ u32x4 act_lds[];   // ACT: M rows of nvec+1 vectors
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<0>) .. f(integral_constant<N-1>), in order
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
-  const int lane = threadIdx.x;
-  const int wave = 0;
-  (void)wave;
+template <int MB, int R, typename OutT>
+__device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict__ ring) {
+  using SH = PanelShape<MB, R>;
+  constexpr int BN = SH::BN;
+  constexpr int kPP = SH::kPP;
+  constexpr int kSlot = SH::slot_elems;
+  constexpr int G = SH::step_loads;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
@@ -1270,173 +1332,187 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
   decode_tile(a, BN, tile, rank);
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
-  if (tile * BN >= a.N) return;
+  if (tile * BN >= a.N) return;        // a whole workgroup past the end (grid padding)
   const int n0 = tile * BN;
+  const int nw = n0 + 16 * wave;       // this wavefront's first column
   const int nvec = a.nvec;
-  const size_t k0 = (size_t)rank * nvec * kVecK;
-  const int nchunks = (nvec + 3) / 4;
-  const int rot = (int)(((unsigned)tile * 5u) % (unsigned)nchunks);
-  const bool whole = nvec % 4 == 0;
-  const int nsteps = (nchunks + U - 1) / U;
+  const int P = nvec / 8;              // steps in the slice; the launch requires nvec % 8 == 0
+  const size_t kw = (size_t)rank * nvec * kVecK;
 
-  const uint16_t* wrow[RG];
+  // Line loads: lane 8q + j fetches 16-byte piece (j - q/2) mod 8 of row q of
+  // an 8-row piece and lands at position j of that row in LDS, so that the
+  // MFMA-layout reads (16 rows at one K offset) fall in distinct banks.
+  const int qr = lane >> 3;
+  const int piece = ((lane & 7) - (qr >> 1)) & 7;
+  // Weight sources: row 8i + qr of this wavefront's 16, rotated piece.
+  const uint16_t* wsrc[2];
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    int n = n0 + 16 * rg + l16;
+  for (int i = 0; i < 2; ++i) {
+    int n = nw + 8 * i + qr;
     n = n < a.N ? n : a.N - 1;
-    wrow[rg] = a.W + (size_t)n * a.K + k0;
+    wsrc[i] = a.W + (size_t)n * a.K + kw + piece * kVecK;
   }
-  const uint16_t* arow[MB];
-  int arow_lds[MB];
-  bool a_ok[MB];
+  // This wavefront's panel pieces: j = wave + 4t (clamped: with MB 3 the
+  // last piece is loaded by more than one wavefront, with identical data,
+  // and every copy lands before the barrier that publishes the stage).
+  // Piece j holds activation rows 8j .. 8j+7; rows >= M read row M-1: MFMA
+  // output rows are independent and rows >= M are never stored.
+  const uint16_t* asrc[SH::a_loads];
+  int apos[SH::a_loads];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) {
-    const int m = 16 * b + l16;
-    a_ok[b] = m < a.M;
-    arow[b] = a.A + (size_t)(a_ok[b] ? m : 0) * a.K + k0;
-    arow_lds[b] = (a_ok[b] ? m : 0) * (nvec + 1);
+  for (int t = 0; t < SH::a_loads; ++t) {
+    int j = wave + kWaves * t;
+    j = j < 2 * MB ? j : 2 * MB - 1;
+    int m = 8 * j + qr;
+    m = m < a.M ? m : a.M - 1;
+    asrc[t] = a.A + (size_t)m * a.K + kw + piece * kVecK;
+    apos[t] = kWaves * SH::w_slot + j * kPP;
   }
-
-  LOWM_STALL(kSiteEntry, 0);
-  if constexpr (ACT) {
-    // the activation slice to LDS, 1 KB pieces; read back only after the
-    // explicit wait below the prologue (the compiler does not order a read
-    // of LDS after a direct-to-LDS load that writes it)
-    const int ppr = nvec / 64;
-    const int total = a.M * ppr;
-    for (int idx = 0; idx < total; ++idx) {
-      const int m = idx / ppr, p = idx - (idx / ppr) * ppr;
-      __builtin_amdgcn_global_load_lds(
-          a.A + (size_t)m * a.K + k0 + p * 512 + lane * kVecK,
-          (__attribute__((address_space(3))) void*)(act_lds + m * (nvec + 1) + p * 64), 16, 0, 0);
-    }
-  }
-
-  // chunk c of the slice in this tile's rotated order; -1 past the end
-  auto phys = [&](int c) {
-    return c < nchunks ? (c + rot < nchunks ? c + rot : c + rot - nchunks) : -1;
-  };
-  auto voff = [&](int v) { return (v < nvec ? v : nvec - 1) * kVecK; };
-
-  f32x4 acc[2][RG][MB];
+  // MFMA-layout read offsets within a pair of 8-row pieces: row l16, piece 4c+g.
+  int rpos[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-      for (int b = 0; b < MB; ++b) acc[h][rg][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < 2; ++c)
+    rpos[c] = (l16 >> 3) * kPP + (l16 & 7) * 8 + ((4 * c + g + ((l16 & 7) >> 1)) & 7);
 
-  u32x4 wreg[NS][U][RG];
-  u32x4 areg[ACT ? 1 : NS][U][MB];
+  f32x4 acc[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto issue = [&](auto slot_c, int s) {
+  auto slot_ptr = [&](int sl) -> u32x4* { return ring + sl * kSlot; };
+  // Step p's loads into slot SL: this wavefront's two weight pieces, then
+  // its share of the panel.
+  auto issue = [&](auto slot_c, int p) {
     constexpr int SL = decltype(slot_c)::value;
+    u32x4* slot = slot_ptr(SL);
+    const size_t off = (size_t)p * 64;
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int p = phys(s * U + j);
-      const int off = voff((p < 0 ? nchunks - 1 : p) * 4 + g);
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(
+          wsrc[i] + off,
+          (__attribute__((address_space(3))) void*)(slot + wave * SH::w_slot + i * kPP), 16, 0,
+          kStreamAux);
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) wreg[SL][j][rg] = load16(wrow[rg] + off);
-      if constexpr (!ACT) {
-#pragma unroll
-        for (int b = 0; b < MB; ++b) areg[SL][j][b] = load16(arow[b] + off);
-      }
-    }
+    for (int t = 0; t < SH::a_loads; ++t)
+      __builtin_amdgcn_global_load_lds(asrc[t] + off,
+                                       (__attribute__((address_space(3))) void*)(slot + apos[t]),
+                                       16, 0, 0);
     pin_issue();
   };
-
-  auto compute_impl = [&](auto slot_c, auto mask_c, int s) {
+  // Step p out of slot SL (= p mod R).  YOUNGER: how many later steps'
+  // loads may still be in flight once step p's have landed; REFILL: whether
+  // step p+R-1 exists (both compile-time, so that every wait count is a
+  // constant and the compiler adds none of its own).
+  auto step = [&](auto slot_c, auto younger_c, auto refill_c, int p) {
     constexpr int SL = decltype(slot_c)::value;
-    constexpr bool MASK = decltype(mask_c)::value;
+    // this wavefront's loads of step p have landed ...
+    wait_vmcnt<decltype(younger_c)::value * G>();
+    // ... and after the barrier every wavefront's have, and every wavefront
+    // has finished reading step p-1's slot
+    barrier_keep_loads();
+    LOWM_STALL(kSiteStageRead, p);
+    if (p == 0) LOWM_TRACE(kTraceFirstStage);
+    if constexpr (decltype(refill_c)::value)
+      issue(std::integral_constant<int, (SL + R - 1) % R>{}, p + R - 1);
+    const u32x4* slot = slot_ptr(SL);
+    u32x4 v[2 + 2 * MB];                    // weight chunks 0, 1, then panel (c, b)
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int p = phys(s * U + j);
-      const int v = p * 4 + g;
-      bool v_ok = true;
-      if constexpr (MASK) v_ok = p >= 0 && v < nvec;
+    for (int c = 0; c < 2; ++c) v[c] = lds_read_opaque(slot + wave * SH::w_slot + rpos[c]);
 #pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        u32x4 av;
-        if constexpr (ACT) av = act_lds[arow_lds[b] + (v_ok ? v : 0)];
-        else av = areg[SL][j][b];
-        av = (a_ok[b] && v_ok) ? av : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          u32x4 wv = wreg[SL][j][rg];
-          if constexpr (MASK) wv = v_ok ? wv : u32x4{0u, 0u, 0u, 0u};
-          acc[j & 1][rg][b] = mfma(av, wv, acc[j & 1][rg][b]);
-        }
-      }
-    }
-  };
-  auto step = [&](auto slot_c, int s) {
-    constexpr int SL = decltype(slot_c)::value;
-    constexpr int NEXT = (SL + NS - 1) % NS;
-    issue(std::integral_constant<int, NEXT>{}, s + NS - 1);
-    if (whole && (s + 1) * U <= nchunks)
-      compute_impl(slot_c, std::false_type{}, s);
-    else
-      compute_impl(slot_c, std::true_type{}, s);
-  };
-
-  issue(std::integral_constant<int, 0>{}, 0);
-  if constexpr (NS > 2) issue(std::integral_constant<int, 1>{}, 1);
-  if constexpr (NS > 3) issue(std::integral_constant<int, 2>{}, 2);
-  if constexpr (ACT) {
-    // The activation pieces went out before the NS-1 prologue groups: once
-    // at most those groups' loads are outstanding, the pieces are in LDS.
-    wait_vmcnt<(NS - 1) * U * RG>();
-  }
-  for (int s = 0; s < nsteps; s += NS) {
-    step(std::integral_constant<int, 0>{}, s);
-    step(std::integral_constant<int, 1>{}, s + 1);
-    if constexpr (NS > 2) step(std::integral_constant<int, 2>{}, s + 2);
-    if constexpr (NS > 3) step(std::integral_constant<int, 3>{}, s + 3);
-  }
-  wait_vmcnt0();
-  LOWM_TRACE(kTraceLoopEnd);
-
-  // This lane's sums: block b, register i is D[4g+i][l16] = C[16b+4g+i][n0+16rg+l16].
-  f32x4 sum[RG][MB];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-    for (int b = 0; b < MB; ++b) sum[rg][b] = acc[0][rg][b] + acc[1][rg][b];
-
-  if (a.S == 1) {
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int b = 0; b < MB; ++b)
+        v[2 + c * MB + b] = lds_read_opaque(slot + kWaves * SH::w_slot + 2 * b * kPP + rpos[c]);
+    lds_wait(v);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * b + 4 * g + i, n = n0 + 16 * rg + l16;
-          if (m < a.M && n < a.N) store_out<OutT>(a, m, n, sum[rg][b][i]);
-        }
-    publish_flags<RG, OutT>(a, n0, lane);
-    LOWM_TRACE(kTraceEnd);
-    return;
-  }
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[b] = mfma(v[2 + c * MB + b], v[c], acc[b]);
+  };
 
-  // a4: publish (device-scope stores, all acknowledged before the arrival)
-  LOWM_STALL(kSitePublish, 0);
-  const int E = a.M * BN;
-  uint32_t* slots = a.part + (size_t)tile * a.S * E;
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+  LOWM_STALL(kSiteEntry, 0);
+  // Steady state: whole ring cycles of R steps in which every step refills
+  // the slot its predecessor read, so R-1 steps are always in flight and
+  // every wait count is the same constant.  The first cycle runs before the
+  // loop, after an unconditional prologue of R-1 steps, and the last
+  // REM = P - p0 steps (R-1 .. 2R-2) run as straight-line code, one sequence
+  // per REM: every issue is then unconditional where it happens.
+  using T = std::true_type;
+  auto cycle = [&](int p0) {
+    static_for<R>([&](auto s_c) {
+      step(s_c, std::integral_constant<int, R - 2>{}, T{}, p0 + decltype(s_c)::value);
+    });
+  };
+  auto tail = [&](auto rem_c, int p0) {
+    constexpr int REM = decltype(rem_c)::value;
+    static_for<REM>([&](auto i_c) {
+      constexpr int I = decltype(i_c)::value;
+      constexpr int YOUNGER = (REM - 1 - I) < (R - 2) ? (REM - 1 - I) : (R - 2);
+      step(std::integral_constant<int, I % R>{},
+           std::integral_constant<int, YOUNGER>{},
+           std::integral_constant<bool, (I + R - 1 < REM)>{}, p0 + I);
+    });
+  };
+  int p0 = 0;
+  if (P >= 2 * R - 1) {
+    static_for<R - 1>([&](auto s_c) { issue(s_c, decltype(s_c)::value); });
+    cycle(0);
+    for (p0 = R; p0 + 2 * R - 1 <= P; p0 += R) cycle(p0);
+  } else {
+    // fewer steps than a prologue plus a cycle: issue what exists
+    static_for<R - 1>([&](auto s_c) {
+      if (decltype(s_c)::value < P) issue(s_c, decltype(s_c)::value);
+    });
+  }
+  // p0 is a multiple of R, so the tail's slots start at 0
+  static_assert(2 * R - 2 <= 14, "the tail covers at most 14 steps");
+  switch (P - p0) {
+#define LOWM_PANEL_TAIL(n) \
+    case n: if constexpr (n <= 2 * R - 2) tail(std::integral_constant<int, n>{}, p0); break;
+    LOWM_PANEL_TAIL(1) LOWM_PANEL_TAIL(2) LOWM_PANEL_TAIL(3) LOWM_PANEL_TAIL(4)
+    LOWM_PANEL_TAIL(5) LOWM_PANEL_TAIL(6) LOWM_PANEL_TAIL(7) LOWM_PANEL_TAIL(8)
+    LOWM_PANEL_TAIL(9) LOWM_PANEL_TAIL(10) LOWM_PANEL_TAIL(11) LOWM_PANEL_TAIL(12)
+    LOWM_PANEL_TAIL(13) LOWM_PANEL_TAIL(14)
+#undef LOWM_PANEL_TAIL
+    default: break;
+  }
+  mfma_settle(acc);
+  LOWM_TRACE(kTraceLoopEnd);
+
+  if (nw >= a.N) return;               // this wavefront's columns lie past the end of C
+  // This lane's sums: block b, register i is C[16b + 4g + i][nw + l16].
+  const int n = nw + l16;
+  if (a.S == 1) {
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16;
-        if (m < a.M) store_slot(slots + (size_t)rank * E + m * BN + nl, enc_partial(sum[rg][b][i]));
+        const int m = 16 * b + 4 * g + i;
+        if (m < a.M && n < a.N) store_out<OutT>(a, m, n, acc[b][i]);
       }
+    publish_flags<1, OutT>(a, nw, lane);
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
+
+  // a4: publish this wavefront's partial strip (element (m, c) at word
+  // 16m + c of the rank's slot), then arrive on the strip's counter.
+  const int strip = nw >> 4;
+  const int E = a.M * 16;
+  uint32_t* slots = a.part + (size_t)strip * a.S * E;
+  uint32_t* ctr = a.ctr + (size_t)strip * kCtrStride;
+  LOWM_STALL(kSitePublish, 0);
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * b + 4 * g + i;
+      if (m < a.M) store_slot(slots + (size_t)rank * E + 16 * m + l16, enc_partial(acc[b][i]));
+    }
   wait_vmcnt0();
   pin_issue();
   uint32_t before = 0;
   if (lane == 0)
-    before = __hip_atomic_fetch_add(a.ctr + (size_t)tile * kCtrStride, 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+    before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
   if (before != (uint32_t)(a.S - 1)) {
@@ -1444,40 +1520,59 @@ __device__ __forceinline__ void wave_tile_body(const Args& a) {
     return;
   }
 
-  // a5/a6: the owner folds in rank order (its own partial from registers)
-  // and returns every slot it read to zero
+  // a5/a6: the owner folds its strip in rank order (its own partial from
+  // registers), one block of 4 rows per lane at a time, stores C and returns
+  // every slot and the counter to zero.  Rows >= M fold row 0 again and keep
+  // nothing.
   LOWM_STALL(kSiteFold, 0);
+  uint32_t* fault = ctr + kFaultWord;
+  float out[MB][4];
+  auto fold_block = [&](auto sn_c, int b) {
+    constexpr int SN = decltype(sn_c)::value;
+    int e[4];
+    float v[4];
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * b + 4 * g + i;
+      e[i] = 16 * (m < a.M ? m : 0) + l16;
+      v[i] = acc[b][i];
+    }
+    if constexpr (SN > 0) fold_owner_n<SN>(slots, E, e, rank, v, fault);
+    else fold_owner_any(slots, E, e, a.S, rank, v, fault);
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
+    for (int i = 0; i < 4; ++i) out[b][i] = v[i];
+  };
+  auto fold_all = [&](auto sn_c) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16;
-        if (m < a.M) sum[rg][b][i] = fold_ranks(slots, E, m * BN + nl, a.S, rank, sum[rg][b][i]);
-      }
+    for (int b = 0; b < MB; ++b) fold_block(sn_c, b);
+  };
+  switch (a.S) {
+    case 2: fold_all(std::integral_constant<int, 2>{}); break;
+    case 3: fold_all(std::integral_constant<int, 3>{}); break;
+    case 4: fold_all(std::integral_constant<int, 4>{}); break;
+    case 8: fold_all(std::integral_constant<int, 8>{}); break;
+    default: fold_all(std::integral_constant<int, 0>{}); break;
+  }
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+  for (int b = 0; b < MB; ++b)
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * b + 4 * g + i, nl = 16 * rg + l16, n = n0 + nl;
-        if (m >= a.M) continue;
-        if (n < a.N) store_out<OutT>(a, m, n, sum[rg][b][i]);
-        clear_slots(slots, E, m * BN + nl, a.S);
-      }
-  publish_flags<RG, OutT>(a, n0, lane);
-  if (lane == 0)
-    __hip_atomic_store(a.ctr + (size_t)tile * kCtrStride, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * b + 4 * g + i;
+      if (m >= a.M) continue;
+      if (n < a.N) store_out<OutT>(a, m, n, out[b][i]);
+      clear_slots(slots, E, 16 * m + l16, a.S);
+    }
+  publish_flags<1, OutT>(a, nw, lane);
+  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   LOWM_TRACE(kTraceEnd);
 }
 
-template <int MB, int RG, int U, int NS, int ACT, typename OutT>
-__global__ __launch_bounds__(kWave) void lowm_wave_kernel(Args a, Batch bt) {
+template <int MB, int R, typename OutT>
+__global__ __launch_bounds__(kThreads) void lowm_panel_kernel(Args a0, Batch bt) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  wave_tile_body<MB, RG, U, NS, ACT, OutT>(gemm_args(a, bt));
+  const Args a = gemm_args(a0, bt);
+  __shared__ u32x4 ring[R * PanelShape<MB, R>::slot_elems];
+  panel_tile_body<MB, R, OutT>(a, ring);
 #endif
 }
 
@@ -1491,21 +1586,9 @@ __global__ __launch_bounds__(kThreads) void lowm_splitk_kernel(Args a, Batch bt)
 }
 
 // ---------------------------------------------------------------------------
-// host side
+// Instantiation: the kernel of (MB, RG, variant VI, activation mode ACT,
+// output kind OutT), or nullptr where the build provides none.
 // ---------------------------------------------------------------------------
-struct Variant {
-  int stage, unroll, stages;
-};
-// The register/LDS variants this build provides.
-constexpr Variant kVariants[] = {
-    {kStageLds, 4, 2},  {kStageLds, 4, 3},  {kStageReg, 8, 2},  {kStageReg, 4, 3},
-    {kStageReg, 4, 4},  {kStageReg, 16, 2}, {kStageReg, 4, 2},  {kStageWave, 4, 4},
-    {kStageWave, 8, 2}, {kStageLine, 2, 2}, {kStageLine, 2, 3}, {kStageLine, 2, 4},
-};
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-
-typedef void (*KernelFn)(Args, Batch);
-
 template <int MB, int RG, int VI, int ACT, typename OutT>
 KernelFn kernel_for() {
   constexpr Variant v = kVariants[VI];
@@ -1515,12 +1598,13 @@ KernelFn kernel_for() {
       return lowm_line_kernel<MB, RG, v.stages, OutT>;
     else
       return nullptr;
-  } else if constexpr (v.stage == kStageWave) {
-    if constexpr (WaveShape<MB, RG, v.unroll, v.stages, ACT>::valid)
-      return lowm_wave_kernel<MB, RG, v.unroll, v.stages, ACT, OutT>;
+  } else if constexpr (v.stage == kStagePanel) {
+    // 64-row tiles (16 rows per wavefront), activation panel in LDS
+    if constexpr (ACT == 0 && RG == 4 && PanelShape<MB, v.stages>::valid)
+      return lowm_panel_kernel<MB, v.stages, OutT>;
     else
       return nullptr;
-  } else if constexpr (Shape<MB, RG, v.stage, v.unroll, v.stages, ACT>::valid) {
+  } else if constexpr (RG <= 2 && Shape<MB, RG, v.stage, v.unroll, v.stages, ACT>::valid) {
     return lowm_splitk_kernel<MB, RG, v.stage, v.unroll, v.stages, ACT, OutT>;
   } else {
     return nullptr;
@@ -1531,21 +1615,6 @@ template <int MB, int RG, int ACT, typename OutT, int... VI>
 void fill_row(KernelFn* row, std::integer_sequence<int, VI...>) {
   ((row[VI] = kernel_for<MB, RG, VI, ACT, OutT>()), ...);
 }
-
-// Rows per tile the build provides: 16 * RG for RG in kRowGroups.
-constexpr int kRowGroups[] = {1, 2, 4};
-constexpr int kNumRowGroups = sizeof(kRowGroups) / sizeof(kRowGroups[0]);
-constexpr int rg_index(int rg) {
-  for (int i = 0; i < kNumRowGroups; ++i)
-    if (kRowGroups[i] == rg) return i;
-  return -1;
-}
-
-// table[out][act][MB-1][rg_index][variant]; out 0 bf16, 1 fp32, 2 bf16 + push
-enum OutKind : int { kOutBf16 = 0, kOutF32 = 1, kOutPush = 2, kNumOutKinds = 3 };
-struct Table {
-  KernelFn fn[kNumOutKinds][2][4][kNumRowGroups][kNumVariants];
-};
 template <typename OutT, int MB, int RG>
 void fill_one(Table& t, int out) {
   constexpr int ri = rg_index(RG);
@@ -1558,6 +1627,7 @@ void fill_mb(Table& t, int out) {
   fill_one<OutT, MB, 2>(t, out);
   fill_one<OutT, MB, 4>(t, out);
 }
+// Every kernel of output kind OutT into row `out` of the table.
 template <typename OutT>
 void fill_out(Table& t, int out) {
   fill_mb<OutT, 1>(t, out);
@@ -1565,508 +1635,5 @@ void fill_out(Table& t, int out) {
   fill_mb<OutT, 3>(t, out);
   fill_mb<OutT, 4>(t, out);
 }
-const Table& table() {
-  static const Table t = [] {
-    Table x{};
-    fill_out<__bf16>(x, kOutBf16);
-    fill_out<float>(x, kOutF32);
-    fill_out<PushBf16>(x, kOutPush);
-    return x;
-  }();
-  return t;
-}
-
-thread_local int g_last_hip_error = 0;
-StressArgs g_stress = {0u, -1, -1, 0, 0, -1, 0u, nullptr};
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-int check_sizes(int M, int N, int K, int S) {
-  if (M <= 0 || N <= 0 || K <= 0 || S < 1) return LOWM_ERR_INVALID_ARG;
-  if (M > LOWM_MAX_M || S > LOWM_MAX_SPLIT_K) return LOWM_ERR_UNSUPPORTED;
-  if (K % (kVecK * S) != 0) return LOWM_ERR_UNSUPPORTED;
-  return LOWM_OK;
-}
-
-size_t counter_bytes(int N) { return (size_t)4 * kCtrStride * ((N + 15) / 16); }
-// Every tile width 16*RG divides this, so tiles * BN <= round_up(N, kPartialPad).
-constexpr size_t kPartialPad = 64;
-
-int variant_index(const lowm_tactic& t) {
-  for (int i = 0; i < kNumVariants; ++i)
-    if (kVariants[i].stage == t.stage && kVariants[i].unroll == t.unroll &&
-        kVariants[i].stages == t.stages)
-      return i;
-  return -1;
-}
-
-int rows_index(int rows) { return rows % 16 == 0 ? rg_index(rows / 16) : -1; }
-
-int threads_of(const lowm_tactic& t) { return t.stage == kStageWave ? kWave : kThreads; }
-
-KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t, bool push = false) {
-  if (t.waves != (t.stage == kStageWave ? 1 : kWaves)) return nullptr;
-  const int ri = rows_index(t.rows);
-  const int vi = variant_index(t);
-  if (ri < 0 || vi < 0 || M < 1 || M > LOWM_MAX_M) return nullptr;
-  return table().fn[push ? kOutPush : f32out ? kOutF32 : kOutBf16][act][(M + 15) / 16 - 1][ri][vi];
-}
-
-// Largest activation slice staged in LDS (bytes, padding included).
-constexpr size_t kActLdsMax = 48 * 1024;
-size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
-
-// Default tactic.  Where the K slice is whole 64-K line pairs per wavefront
-// (K / split_k % 256 == 0) and M <= 32: line-pair tiles of 16 rows, a ring of
-// 4 slots for M <= 4 with 8..15 pairs per wavefront and of 2 otherwise; not
-// for M > 16 with 16 or more pairs, where the register ring below is faster.
-// Measured on MI355X at N 6144, K 4096, M 1..32, split_k 1..8, and at
-// N 2304 K 12288 split_k 4 and N 49152 K 4096 split_k 2: the line tiles
-// beat the register ring by 3-30 % everywhere else.
-// Otherwise tiles of 16 weight rows for M <= 16 and 32 above (two row
-// groups share each activation load) in a register ring: each of the four
-// wavefronts streams cpw = ceil(chunks / 4) contiguous chunks of its slice.
-// When cpw <= 16 the best ring issues the whole range in its first stage
-// (unroll = the smallest power of two >= cpw, 2 stages); for longer ranges a
-// 4-chunk, 2-stage ring beats deeper ones.  Fall back to other rings, then
-// the single-wavefront and LDS variants, when the build has no such
-// instantiation for this M.
-int pick(int M, int N, int K, int S, lowm_tactic* t) {
-  const int rc = check_sizes(M, N, K, S);
-  if (rc != LOWM_OK) return rc;
-  const int nvec = K / S / kVecK;
-  const int cpw = ((nvec + 3) / 4 + kWaves - 1) / kWaves;
-  const int act = (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) ? 1 : 0;
-  int first_unroll = 4;
-  if (cpw <= 16) {
-    while (first_unroll < cpw) first_unroll *= 2;
-  }
-  const Variant first = {kStageReg, first_unroll, 2};
-  static const Variant others[] = {{kStageReg, 4, 2},  {kStageReg, 4, 3},  {kStageReg, 8, 2},
-                                   {kStageWave, 4, 4}, {kStageWave, 8, 2}, {kStageLds, 4, 2},
-                                   {kStageLds, 4, 3}};
-  t->rows = M <= 16 ? 16 : 32;
-  // The launch stages the activation slice in LDS when `act` is 1 and the
-  // build has that instantiation, else it loads activation operands from L2;
-  // the tactic must exist in the mode the launch will use.
-  auto provides = [&](const Variant& v) {
-    t->stage = v.stage;
-    t->unroll = v.unroll;
-    t->stages = v.stages;
-    t->waves = v.stage == kStageWave ? 1 : kWaves;
-    for (int f = 0; f < 2; ++f) {
-      const bool f32 = f == 1;
-      if (!(act && lookup(f32, 1, M, *t)) && !lookup(f32, 0, M, *t)) return false;
-    }
-    return true;
-  };
-  if (nvec % 32 == 0 && M <= 32) {
-    const int pairs = nvec / 32;   // line pairs per wavefront
-    // Measured on MI355X: 32-row line tiles beat 16-row ones only without
-    // split-K, for 5..16 activation rows, 16 line pairs per wavefront and at
-    // least 192 tiles (M 16, N 6144, K 4096: 12.3 vs 14.4 us; M 16, N 24576:
-    // 32.9 vs 40.5); with split_k 2..8, other slice lengths or fewer tiles
-    // they lose.
-    if (S == 1 && M > 4 && M <= 16 && pairs == 16 && (N + 31) / 32 >= 192) {
-      t->rows = 32;
-      if (provides({kStageLine, 2, 2})) return LOWM_OK;
-    }
-    if (!(M > 16 && pairs >= 16)) {
-      const int ring = (M <= 4 && pairs >= 8 && pairs < 16) ? 4 : 2;
-      t->rows = 16;
-      if (provides({kStageLine, 2, ring})) return LOWM_OK;
-    }
-  }
-  t->rows = M <= 16 ? 16 : 32;
-  if (provides(first)) return LOWM_OK;
-  for (const Variant& v : others)
-    if (provides(v)) return LOWM_OK;
-  return LOWM_ERR_UNSUPPORTED;
-}
-
-// split_k for a shape, from a table of the fastest measured on MI355X (default
-// tactic for each split_k, W streamed from HBM): M 4 and 16, N 768 .. 24576,
-// K 2048 .. 16384, split_k 1, 2, 4, 8.  A shape takes its nearest grid point
-// in log2 N and log2 K; M <= 8 uses the M 4 row, larger M the M 16 row.  On
-// the grid every entry is the fastest split_k; off it, the neighbours were
-// within 10 % of each other's best.  split_k pays when the tiles are few and
-// K is long; for M 16 the larger partials make it pay less often.
-constexpr unsigned char kBestSplit[2][6][4] = {
-    // M <= 8            K: 2048 4096 8192 16384
-    {{1, 4, 4, 8},    // N 768
-     {2, 2, 4, 4},    // N 1536
-     {1, 2, 2, 4},    // N 3072
-     {1, 2, 2, 8},    // N 6144
-     {1, 1, 2, 8},    // N 12288
-     {1, 1, 2, 8}},   // N 24576
-    // M > 8
-    {{1, 4, 4, 4},
-     {1, 2, 8, 8},
-     {1, 1, 4, 4},
-     {1, 1, 2, 4},
-     {1, 1, 1, 1},
-     {1, 1, 1, 1}}};
-
-int nearest_log2_index(double x, double base, int last) {
-  const int i = (int)floor(log2(x / base) + 0.5);
-  return i < 0 ? 0 : (i > last ? last : i);
-}
-
-int pick_split(int M, int N, int K, int* split_k) {
-  if (!split_k) return LOWM_ERR_INVALID_ARG;
-  int rc = check_sizes(M, N, K, 1);
-  if (rc != LOWM_OK) return rc;
-  int S = kBestSplit[M <= 8 ? 0 : 1][nearest_log2_index(N, 768.0, 5)]
-                    [nearest_log2_index(K, 2048.0, 3)];
-  // the largest power of two <= S that K allows (a whole number of 16-byte
-  // vectors per slice), preferring slices that are whole line pairs
-  while (S > 1 && K % (kVecK * S) != 0) S /= 2;
-  while (S > 1 && (K / S) % 256 != 0 && K % 256 == 0) S /= 2;
-  *split_k = S;
-  return LOWM_OK;
-}
-
-// The kernel a launch with tactic t runs: the activation slice is staged in
-// LDS when it is small and whole 1 KB pieces (and the build has that
-// instantiation); otherwise the wavefronts load activation operands from L2.
-KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_t* dyn_lds,
-                       bool push = false) {
-  *dyn_lds = 0;
-  // line-pair tiles stream whole 64-K line pairs per wavefront
-  if (t.stage == kStageLine && nvec % 32 != 0) return nullptr;
-  if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
-    if (KernelFn fn = lookup(f32out, 1, M, t, push)) {
-      *dyn_lds = act_lds_bytes(M, nvec);
-      return fn;
-    }
-  }
-  *dyn_lds = 0;
-  return lookup(f32out, 0, M, t, push);
-}
-
-size_t workspace_bytes(int M, int N, int K, int S) {
-  if (check_sizes(M, N, K, S) != LOWM_OK || S == 1) return 0;
-  // counters for up to ceil(N/16) tiles, then [tiles][split_k][M][BN] fp32
-  // partials; tiles * BN never exceeds N rounded up to 64, a multiple of
-  // every tile width.  Both parts are multiples of 256 bytes.
-  return counter_bytes(N) + (size_t)S * (size_t)M * round_up((size_t)N, kPartialPad) * sizeof(float);
-}
-
-// The push epilogue of a single-GEMM launch (bf16 output).
-struct PushSpec {
-  void* dst;
-  int ld;
-  uint32_t* flags;
-  uint32_t value;
-};
-
-// [lo, hi) of the bytes a row-major [rows, cols] array with row pitch ld
-// elements of `elem` bytes spans.
-inline void byte_span(const void* p, int rows, int cols, int ld, size_t elem, uintptr_t* lo,
-                      uintptr_t* hi) {
-  *lo = (uintptr_t)p;
-  *hi = *lo + ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * elem;
-}
-
-int check_push(const PushSpec& p, const void* C, int M, int N) {
-  if (!p.dst || !p.flags || p.value == 0 || p.ld < N) return LOWM_ERR_INVALID_ARG;
-  if (((uintptr_t)p.dst & 1) || ((uintptr_t)p.flags & 3)) return LOWM_ERR_UNSUPPORTED;
-  uintptr_t c0, c1, d0, d1, f0, f1;
-  byte_span(C, M, N, N, 2, &c0, &c1);
-  byte_span(p.dst, M, N, p.ld, 2, &d0, &d1);
-  byte_span(p.flags, 1, (N + 15) / 16, 0, 4, &f0, &f1);
-  auto overlap = [](uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
-    return a0 < b1 && b0 < a1;
-  };
-  if (overlap(c0, c1, d0, d1) || overlap(c0, c1, f0, f1) || overlap(d0, d1, f0, f1))
-    return LOWM_ERR_INVALID_ARG;
-  return LOWM_OK;
-}
-
-// One launch of `count` GEMMs sharing M, K, split_k, the output type and the
-// tactic; the single-GEMM entry points are the count == 1 case.  GEMM g's
-// workspace follows GEMM g-1's (each is workspace_bytes of its own sizes).
-// `push` (single bf16 GEMM only) adds the push epilogue.
-int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int K, int S,
-                 void* workspace, hipStream_t stream, const lowm_tactic* tactic,
-                 const PushSpec* push = nullptr) {
-  if (!gemms || count < 1) return LOWM_ERR_INVALID_ARG;
-  if (count > kMaxBatch) return LOWM_ERR_UNSUPPORTED;
-  if (push && (count != 1 || f32out)) return LOWM_ERR_INVALID_ARG;
-  for (int g = 0; g < count; ++g)
-    if (!gemms[g].A || !gemms[g].W || !gemms[g].C) return LOWM_ERR_INVALID_ARG;
-  int rc = LOWM_OK;
-  for (int g = 0; g < count; ++g) {
-    rc = check_sizes(M, gemms[g].N, K, S);
-    if (rc != LOWM_OK) return rc;
-  }
-  if (S > 1 && !workspace) return LOWM_ERR_WORKSPACE;
-  for (int g = 0; g < count; ++g) {
-    if (((uintptr_t)gemms[g].A | (uintptr_t)gemms[g].W) & 15) return LOWM_ERR_UNSUPPORTED;
-    if ((uintptr_t)gemms[g].C & (f32out ? 3 : 1)) return LOWM_ERR_UNSUPPORTED;
-  }
-  if (S > 1 && ((uintptr_t)workspace & 15)) return LOWM_ERR_UNSUPPORTED;
-  if (push) {
-    rc = check_push(*push, gemms[0].C, M, gemms[0].N);
-    if (rc != LOWM_OK) return rc;
-  }
-
-  lowm_tactic t;
-  if (tactic) {
-    t = *tactic;
-  } else {
-    // One tactic serves every GEMM of the launch: pick it for the narrowest
-    // (the only rule that depends on N asks for enough tiles).
-    int n_min = gemms[0].N;
-    for (int g = 1; g < count; ++g) n_min = gemms[g].N < n_min ? gemms[g].N : n_min;
-    rc = pick(M, n_min, K, S, &t);
-    if (rc != LOWM_OK) return rc;
-  }
-  const int nvec = K / S / kVecK;
-  size_t dyn_lds = 0;
-  const KernelFn fn = select_kernel(f32out, M, nvec, t, &dyn_lds, push != nullptr);
-  if (!fn) return LOWM_ERR_UNSUPPORTED;
-
-  const int BN = t.rows;
-  Batch bt{};
-  size_t grid = 0, ws_off = 0;
-  for (int g = 0; g < count; ++g) {
-    GemmSlot& sl = bt.g[g];
-    const int N = gemms[g].N;
-    sl.A = static_cast<const uint16_t*>(gemms[g].A);
-    sl.W = static_cast<const uint16_t*>(gemms[g].W);
-    sl.C = gemms[g].C;
-    sl.N = N;
-    char* ws = static_cast<char*>(workspace) + ws_off;
-    sl.ctr = S > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
-    sl.part = S > 1 ? reinterpret_cast<uint32_t*>(ws + counter_bytes(N)) : nullptr;
-    ws_off += workspace_bytes(M, N, K, S);
-    const size_t tiles = (size_t)((N + BN - 1) / BN);
-    grid += round_up(tiles, kXcds) * (size_t)S;
-    if (grid > 0x7fffffffu) return LOWM_ERR_UNSUPPORTED;
-    sl.bid_end = (int)grid;
-  }
-  for (int g = count; g < kMaxBatch; ++g) bt.g[g] = bt.g[count - 1];
-
-  Args a{};
-  a.A = bt.g[0].A;
-  a.W = bt.g[0].W;
-  a.C = bt.g[0].C;
-  a.M = M;
-  a.N = bt.g[0].N;
-  a.K = K;
-  a.S = S;
-  a.nvec = nvec;
-  a.batch = count;
-  a.ctr = bt.g[0].ctr;
-  a.part = bt.g[0].part;
-  a.bid_base = 0;
-  a.push = push ? static_cast<uint16_t*>(push->dst) : nullptr;
-  a.flags = push ? push->flags : nullptr;
-  a.push_ld = push ? push->ld : 0;
-  a.flag_value = push ? push->value : 0u;
-  a.stress = g_stress;
-
-  void* kargs[] = {&a, &bt};
-  hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)grid),
-                                   dim3(threads_of(t)), kargs, dyn_lds, stream);
-  if (err == hipSuccess) err = hipGetLastError();
-  if (err != hipSuccess) {
-    g_last_hip_error = (int)err;
-    return LOWM_ERR_LAUNCH;
-  }
-  return LOWM_OK;
-}
-
-int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int K, int S,
-           void* workspace, hipStream_t stream, const lowm_tactic* tactic,
-           const PushSpec* push = nullptr) {
-  const lowm_gemm_desc one = {A, W, C, N};
-  return launch_batch(&one, 1, f32out, M, K, S, workspace, stream, tactic, push);
-}
-
-// Consumer side of the push epilogue: one wavefront polls the flags with
-// system-scope loads until each holds `value` or `ticks` of the 100 MHz
-// real-time counter have passed, then writes how many flags it did not see
-// set (0: all were).  Every poll of a flag is a fresh load; a flag once seen
-// is not polled again.
-constexpr int kWaitFlagsPerLane = 64;
-constexpr int kMaxWaitFlags = kWave * kWaitFlagsPerLane;
-constexpr uint32_t kMaxWaitUs = 10u * 1000u * 1000u;
-
-__global__ __launch_bounds__(kWave) void lowm_push_wait_kernel(const uint32_t* flags, int n,
-                                                                uint32_t value, uint64_t ticks,
-                                                                int* missing) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const int lane = threadIdx.x;
-  uint64_t pending = 0;   // bit j: flag lane + 64 j not yet seen
-  for (int j = 0; j < kWaitFlagsPerLane; ++j)
-    if (lane + kWave * j < n) pending |= 1ull << j;
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
-    for (int j = 0; j < kWaitFlagsPerLane; ++j) {
-      if (!(pending >> j & 1)) continue;
-      const uint32_t f = __hip_atomic_load(flags + lane + kWave * j, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_SYSTEM);
-      if (f == value) pending &= ~(1ull << j);
-    }
-    if (__all(pending == 0)) break;
-    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
-    __builtin_amdgcn_s_sleep(8);
-  }
-  int left = __popcll(pending);
-  for (int off = kWave / 2; off > 0; off >>= 1) left += __shfl_xor(left, off);
-  if (lane == 0) missing[0] = left;
-#endif
-}
-
-int push_wait(const uint32_t* flags, int n, uint32_t value, uint32_t timeout_us, int* missing,
-              hipStream_t stream) {
-  if (!flags || !missing || n < 1 || value == 0) return LOWM_ERR_INVALID_ARG;
-  if (n > kMaxWaitFlags || timeout_us > kMaxWaitUs) return LOWM_ERR_UNSUPPORTED;
-  if (((uintptr_t)flags & 3) || ((uintptr_t)missing & 3)) return LOWM_ERR_UNSUPPORTED;
-  const uint64_t ticks = (uint64_t)timeout_us * 100u;
-  void* kargs[] = {&flags, &n, &value, const_cast<uint64_t*>(&ticks), &missing};
-  hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&lowm_push_wait_kernel),
-                                   dim3(1), dim3(kWave), kargs, 0, stream);
-  if (err == hipSuccess) err = hipGetLastError();
-  if (err != hipSuccess) {
-    g_last_hip_error = (int)err;
-    return LOWM_ERR_LAUNCH;
-  }
-  return LOWM_OK;
-}
 
 }  // namespace lowm
-
-// ---------------------------------------------------------------------------
-// C ABI
-// ---------------------------------------------------------------------------
-extern "C" {
-
-int lowm_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int split_k,
-                     void* workspace, void* stream) {
-  return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
-                      static_cast<hipStream_t>(stream), nullptr);
-}
-
-int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C, int M, int N, int K,
-                            int split_k, void* workspace, void* stream) {
-  return lowm::launch(A, W, C, true, M, N, K, split_k, workspace,
-                      static_cast<hipStream_t>(stream), nullptr);
-}
-
-int lowm_gemm_splitk_ex(const void* A, const void* W, void* C, int M, int N, int K,
-                        int split_k, void* workspace, void* stream, const lowm_tactic* tactic) {
-  return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
-                      static_cast<hipStream_t>(stream), tactic);
-}
-
-int lowm_gemm_splitk_f32out_ex(const void* A, const void* W, float* C, int M, int N, int K,
-                               int split_k, void* workspace, void* stream,
-                               const lowm_tactic* tactic) {
-  return lowm::launch(A, W, C, true, M, N, K, split_k, workspace,
-                      static_cast<hipStream_t>(stream), tactic);
-}
-
-size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k) {
-  return lowm::workspace_bytes(M, N, K, split_k);
-}
-
-int lowm_gemm_splitk_push(const void* A, const void* W, void* C, int M, int N, int K,
-                          int split_k, void* workspace, void* push, int push_ld,
-                          uint32_t* flags, uint32_t flag_value, void* stream,
-                          const lowm_tactic* tactic) {
-  const lowm::PushSpec ps = {push, push_ld, flags, flag_value};
-  return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
-                      static_cast<hipStream_t>(stream), tactic, &ps);
-}
-
-int lowm_push_wait(const uint32_t* flags, int n_flags, uint32_t flag_value,
-                   uint32_t timeout_us, int* missing, void* stream) {
-  return lowm::push_wait(flags, n_flags, flag_value, timeout_us, missing,
-                         static_cast<hipStream_t>(stream));
-}
-
-int lowm_gemm_splitk_batched(const lowm_gemm_desc* gemms, int count, int M, int K,
-                             int split_k, void* workspace, void* stream) {
-  return lowm::launch_batch(gemms, count, false, M, K, split_k, workspace,
-                            static_cast<hipStream_t>(stream), nullptr);
-}
-
-size_t lowm_gemm_splitk_batched_workspace_bytes(const lowm_gemm_desc* gemms, int count, int M,
-                                                int K, int split_k) {
-  if (!gemms || count < 1 || count > LOWM_MAX_BATCH) return 0;
-  size_t total = 0;
-  for (int g = 0; g < count; ++g) {
-    if (lowm::check_sizes(M, gemms[g].N, K, split_k) != LOWM_OK) return 0;
-    total += lowm::workspace_bytes(M, gemms[g].N, K, split_k);
-  }
-  return total;
-}
-
-int lowm_pick_split_k(int M, int N, int K, int* split_k) {
-  return lowm::pick_split(M, N, K, split_k);
-}
-
-int lowm_check_launch(int M, int N, int K, int split_k, int f32out, const lowm_tactic* tactic) {
-  int rc = lowm::check_sizes(M, N, K, split_k);
-  if (rc != LOWM_OK) return rc;
-  lowm_tactic t;
-  if (tactic) {
-    t = *tactic;
-  } else {
-    rc = lowm::pick(M, N, K, split_k, &t);
-    if (rc != LOWM_OK) return rc;
-  }
-  size_t dyn = 0;
-  return lowm::select_kernel(f32out != 0, M, K / split_k / lowm::kVecK, t, &dyn)
-             ? LOWM_OK
-             : LOWM_ERR_UNSUPPORTED;
-}
-
-int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out) {
-  if (!out) return LOWM_ERR_INVALID_ARG;
-  return lowm::pick(M, N, K, split_k, out);
-}
-
-const char* lowm_strerror(int code) {
-  switch (code) {
-    case LOWM_OK: return "success";
-    case LOWM_ERR_INVALID_ARG: return "invalid argument (NULL operand, size <= 0, split_k < 1)";
-    case LOWM_ERR_UNSUPPORTED:
-      return "unsupported (M > 64, K not a multiple of 8*split_k, split_k > 256, misaligned "
-             "pointer, or tactic not in this build)";
-    case LOWM_ERR_WORKSPACE: return "split_k > 1 needs a workspace";
-    case LOWM_ERR_LAUNCH: return "kernel launch failed (see lowm_last_hip_error)";
-    default: return "unknown error code";
-  }
-}
-
-int lowm_last_hip_error(void) { return lowm::g_last_hip_error; }
-
-#ifdef LOWM_STRESS
-// Stress build only: where, on whom and how long the kernels stall.  Applies
-// to every later launch from any thread; not thread-safe.
-int lowm_stress_configure(unsigned site_mask, int rank, int wave, int tile_mod, int tile_sel,
-                          int step, unsigned delay_ns) {
-  if (delay_ns > 1000000u) return LOWM_ERR_INVALID_ARG;  // at most 1 ms per stall
-  lowm::g_stress.site_mask = site_mask;
-  lowm::g_stress.rank = rank;
-  lowm::g_stress.wave = wave;
-  lowm::g_stress.tile_mod = tile_mod;
-  lowm::g_stress.tile_sel = tile_sel;
-  lowm::g_stress.step = step;
-  lowm::g_stress.ticks = delay_ns / 10u;  // s_memrealtime: 100 MHz
-  return LOWM_OK;
-}
-
-// Stress build only: record per-workgroup timestamps into `buf` (device
-// memory, 8 uint64 per workgroup of the grid; NULL stops tracing).
-int lowm_stress_trace(void* buf) {
-  lowm::g_stress.trace = static_cast<uint64_t*>(buf);
-  return LOWM_OK;
-}
-#endif
-
-}  // extern "C"

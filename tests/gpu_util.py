@@ -41,17 +41,20 @@ def oracle_result(wl: workloads.Workload):
 
 
 VARIANTS = [("lds", 4, 2), ("lds", 4, 3),
-            ("reg", 8, 2), ("reg", 4, 3), ("reg", 4, 4), ("reg", 16, 2), ("reg", 4, 2),
-            ("wave", 4, 4), ("wave", 8, 2),
+            ("reg", 4, 2), ("reg", 8, 2), ("reg", 16, 2),
             ("line", 2, 2), ("line", 2, 3), ("line", 2, 4)]
+PANEL_RINGS = (3, 4, 6)
 
 
 def all_tactics(M: int):
-    """Every tactic this build provides for M activation rows."""
+    """Every tactic this build may provide for M activation rows (the
+    launch returns LOWM_ERR_UNSUPPORTED for those it lacks)."""
     out = []
-    for rows in (16, 32, 64):
+    for rows in (16, 32):
         for stage, unroll, stages in VARIANTS:
             out.append(binding.tactic(stage, rows, unroll, stages))
+    for ring in PANEL_RINGS:
+        out.append(binding.tactic("panel", 64, 2, ring))
     return out
 
 

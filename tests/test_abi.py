@@ -89,7 +89,7 @@ def test_pick_tactic_is_valid_for_every_workload(lib):
     import workloads
     for wl in workloads.ALL:
         t = lib.pick_tactic(wl.M, wl.N, wl.K, wl.split_k)
-        assert t.rows in (16, 32, 64) and t.waves in (1, 4)
+        assert t.rows in (16, 32, 64) and t.waves == 4
         if t.stage != binding.LOWM_STAGE_LINE:
             assert t.rows >= min(32, 16 * ((wl.M + 15) // 16))
         assert lib.check_launch(wl.M, wl.N, wl.K, wl.split_k, tactic=t) == 0
@@ -101,12 +101,24 @@ def test_pick_prefers_line_pairs_where_measured_faster(lib):
     assert (t.stage, t.rows, t.unroll, t.stages) == (line, 16, 2, 4)
     t = lib.pick_tactic(16, 6144, 4096, 8)       # 2 pairs
     assert (t.stage, t.stages) == (line, 2)
-    t = lib.pick_tactic(32, 6144, 4096, 1)       # M > 16 with 16 pairs: register ring
-    assert t.stage == binding.LOWM_STAGE_REG
     t = lib.pick_tactic(4, 97, 1032, 3)          # ragged K slice: register ring
-    assert t.stage != line
-    t = lib.pick_tactic(64, 6144, 4096, 2)       # M > 32: register ring
-    assert t.stage != line
+    assert t.stage == binding.LOWM_STAGE_REG
+
+
+def test_pick_panel_tiles_above_16_rows(lib):
+    panel = binding.LOWM_STAGE_PANEL
+    for M, N, K, S in [(17, 6144, 4096, 2), (32, 6144, 4096, 1), (64, 6144, 4096, 2),
+                       (64, 49152, 4096, 8), (48, 100, 512, 1)]:
+        t = lib.pick_tactic(M, N, K, S)
+        assert (t.stage, t.rows, t.unroll, t.stages) == (panel, 64, 2, 4), (M, N, K, S, t)
+    # a slice that is not whole 64-K steps: register ring
+    t = lib.pick_tactic(64, 6144, 1032, 3)
+    assert t.stage == binding.LOWM_STAGE_REG
+    # 16 rows or fewer: never panel tiles (the build has none for one row block)
+    for M in (1, 4, 16):
+        assert lib.pick_tactic(M, 6144, 4096, 2).stage != panel
+        assert lib.check_launch(M, 6144, 4096, 2, tactic=binding.tactic("panel", 64, 2, 4)) == \
+            binding.LOWM_ERR_UNSUPPORTED
 
 
 def test_pick_32_row_line_tiles_only_where_measured_faster(lib):

@@ -195,3 +195,30 @@ def test_one_workspace_serves_launches_of_different_shapes(lib):
         got = to_bits(run(lib, A, W, wl.split_k, workspace=shared))
         assert np.array_equal(got, fresh[wl.name]), f"{wl.name} differs on the shared workspace"
         assert not shared.cpu().numpy().any(), f"{wl.name} left the shared workspace non-zero"
+
+
+PANEL_CASES = [  # M, N, K, S: ragged N (partial strips, wavefronts past the end),
+    (17, 130, 640, 5),     # 2 steps per slice (ring not filled), generic split_k fold
+    (33, 77, 512, 2),      # 2 tiles: the second has one partial strip
+    (48, 1000, 1536, 3),   # 3 activation blocks
+    (64, 64, 4096, 8),     # one tile, split_k 8
+    (64, 6200, 2048, 1),   # no split: direct stores
+    (32, 2304, 12288, 4),  # long slices
+]
+
+
+@pytest.mark.parametrize("ring", [3, 4, 6])
+@pytest.mark.parametrize("M,N,K,S", PANEL_CASES)
+def test_panel_tiles(lib, M, N, K, S, ring):
+    """Panel tiles (activation panel shared in LDS, each 16-column strip
+    owned by one wavefront through the exchange) against the oracle."""
+    wl = workloads.Workload(f"panel_{M}_{N}_{K}_{S}", M, N, K, S, seed_a=M + ring, seed_w=N + S)
+    t = sbg.tactic("panel", 64, 2, ring)
+    v = check_random(lib, wl, tactic=t, what=f"panel ring {ring} {M}x{N}x{K} s{S}")
+    assert v is not None, f"panel ring {ring} is not built for M {M}"
+
+
+@pytest.mark.parametrize("wl", [w for w in workloads.sweep() if w.M >= 32], ids=lambda w: w.name)
+def test_panel_tiles_sweep(lib, wl):
+    v = check_random(lib, wl, tactic=sbg.tactic("panel", 64, 2, 4), what=f"panel {wl.name}")
+    assert v is not None

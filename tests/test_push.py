@@ -30,7 +30,7 @@ CASES = [  # M, N, K, split_k
     (1, 2304, 12288, 4),
 ]
 
-TACTICS = [None, ("reg", 16, 4, 2), ("wave", 16, 4, 4), ("lds", 16, 4, 2), ("reg", 32, 4, 2)]
+TACTICS = [None, ("reg", 16, 4, 2), ("panel", 64, 2, 4), ("lds", 16, 4, 2), ("reg", 32, 4, 2)]
 
 
 def window(M, N, dev, off=24, extra=40):

@@ -43,8 +43,11 @@ PLANS = [
     ("publish + fold, every 5th tile", binding.SITE_PUBLISH | binding.SITE_FOLD, -1, -1, 5, 2, -1),
 ]
 
-TACTICS = [None, binding.tactic("lds", 16, 4, 2), binding.tactic("reg", 16, 4, 3),
-           binding.tactic("wave", 16, 4, 4)]
+# (workload, tactic): the default tactic at the headline shape is the line-pair
+# tiles; the panel tiles (the default above 16 rows) run at M 64, split_k 2.
+CASES = [(workloads.HEADLINE, None), (workloads.HEADLINE, binding.tactic("lds", 16, 4, 2)),
+         (workloads.HEADLINE, binding.tactic("reg", 16, 8, 2)),
+         (workloads.by_name("sweep_m64_n6144_k4096_s2"), None)]
 
 
 @pytest.fixture(scope="module")
@@ -62,11 +65,11 @@ def launch(lib, ops, wl, tactic):
     return to_bits(out)
 
 
-@pytest.mark.parametrize("tactic", TACTICS, ids=["default", "lds_ns2", "reg_u4_ns3", "wave_u4_ns4"])
+@pytest.mark.parametrize("case", CASES, ids=["line_default", "lds_ns2", "reg_u8_ns2", "panel_m64"])
 @pytest.mark.parametrize("plan", PLANS, ids=[p[0] for p in PLANS])
-def test_headline_under_stalls(libs, plan, tactic):
+def test_under_stalls(libs, plan, case):
     base, stress = libs
-    wl = workloads.HEADLINE
+    wl, tactic = case
     dev = device()
     A, W = (t.to(dev) for t in inputs(wl))
     ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
