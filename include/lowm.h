@@ -69,6 +69,9 @@ extern "C" {
 #define LOWM_ERR_WORKSPACE (-3)
 /* The kernel launch itself failed; see lowm_last_hip_error(). */
 #define LOWM_ERR_LAUNCH (-4)
+/* lowm_gemm_splitk_noalloc: the sizes need a workspace larger than
+ * LOWM_SCRATCH_BYTES. */
+#define LOWM_ERR_SCRATCH (-5)
 
 /* Largest M the kernels accept. */
 #define LOWM_MAX_M 64
@@ -265,6 +268,29 @@ int lowm_gemm_splitk_push(const void* A, const void* W, void* C, int M, int N, i
  */
 int lowm_push_wait(const uint32_t* flags, int n_flags, uint32_t flag_value,
                    uint32_t timeout_us, int* missing, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the product
+ * of lowm_gemm_splitk, bit for bit the same kernels, tactic and summation
+ * order, with the split-K workspace taken from a buffer built into the
+ * library instead of the caller's.  No hipMalloc, hipFree or other
+ * allocation happens in this call.
+ *
+ * The buffer is a device array of LOWM_SCRATCH_BYTES per GPU, held from the
+ * library's first call on that GPU until the process ends; its device
+ * address is looked up once per GPU (on the device `stream` belongs to).  It
+ * is zero when loaded, and every launch that completes returns every word it
+ * used to zero, so each call finds it clear.  All calls on one GPU share it:
+ * calls that overlap in time on that GPU (two streams, or two threads) race
+ * and must not be issued.  Sizes whose workspace
+ * (lowm_gemm_splitk_workspace_bytes) exceeds LOWM_SCRATCH_BYTES return
+ * LOWM_ERR_SCRATCH before any HIP call; other arguments and errors as
+ * lowm_gemm_splitk.  split_k == 1 uses no workspace.
+ */
+#define LOWM_SCRATCH_BYTES (16u << 20)
+int lowm_gemm_splitk_noalloc(const void* A, const void* W, void* C,
+                             int M, int N, int K, int split_k, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,8 @@ LOWM_ERR_INVALID_ARG = -1
 LOWM_ERR_UNSUPPORTED = -2
 LOWM_ERR_WORKSPACE = -3
 LOWM_ERR_LAUNCH = -4
+LOWM_ERR_SCRATCH = -5
+SCRATCH_BYTES = 16 << 20
 LOWM_STAGE_LDS = 0
 LOWM_STAGE_REG = 1
 LOWM_STAGE_LINE = 3
@@ -109,6 +111,8 @@ class Library:
         lib.lowm_check_launch.restype = _i
         lib.lowm_pick_split_k.argtypes = [_i, _i, _i, ctypes.POINTER(_i)]
         lib.lowm_pick_split_k.restype = _i
+        lib.lowm_gemm_splitk_noalloc.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp]
+        lib.lowm_gemm_splitk_noalloc.restype = _i
         lib.lowm_gemm_splitk_push.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _vp,
                                               ctypes.c_uint32, _vp, ctypes.POINTER(Tactic)]
         lib.lowm_gemm_splitk_push.restype = _i
@@ -181,6 +185,19 @@ class Library:
         rc = self.call_raw(A.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, split_k,
                            ws_ptr, s.cuda_stream, f32out, tactic)
         self.check(rc)
+        return out
+
+    def gemm_noalloc(self, A: torch.Tensor, W: torch.Tensor, split_k: int = 1,
+                     out: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """C = A @ W.T (bf16) through lowm_gemm_splitk_noalloc: the split-K
+        workspace is the library's built-in scratch, so the C call allocates
+        nothing (pass `out` to keep this call allocation-free as well)."""
+        M, N, K = self._operands(A, W)
+        out = self._out(out, M, N, torch.bfloat16, A.device)
+        s = stream if stream is not None else torch.cuda.current_stream(A.device)
+        self.check(self.lib.lowm_gemm_splitk_noalloc(A.data_ptr(), W.data_ptr(), out.data_ptr(),
+                                                     M, N, K, split_k, s.cuda_stream))
         return out
 
     @staticmethod

@@ -9,6 +9,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "lowm_types.h"
 
 namespace lowm {
@@ -333,6 +336,60 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
   return LOWM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Built-in workspace of the no-allocation entry point: a file-scope device
+// array, one copy per GPU the library runs on, held until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// its device address is looked up once per device with hipGetSymbolAddress
+// (with that device current) and only that address is ever passed on.
+// The array is zero when the library is loaded onto a device, and every
+// launch that completes returns every word it used (counters and partial
+// slots) to zero, exactly as with a caller's workspace: each call finds it
+// all zero without any clearing.  Calls that overlap in time on one GPU
+// (two streams) share it and race.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = LOWM_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the device `stream` belongs to.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t err = hipStreamGetDevice(stream, &dev);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return LOWM_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return LOWM_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = 0;
+      err = hipGetDevice(&cur);
+      if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+      if (err == hipSuccess) {
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+          const hipError_t back = hipSetDevice(cur);
+          if (err == hipSuccess) err = back;
+        }
+      }
+      if (err != hipSuccess || !p) {
+        g_last_hip_error = (int)err;
+        return LOWM_ERR_LAUNCH;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return LOWM_OK;
+}
+
 int launch(const void* A, const void* W, void* C, bool f32out, int M, int N, int K, int S,
            void* workspace, hipStream_t stream, const lowm_tactic* tactic,
            const PushSpec* push = nullptr) {
@@ -403,6 +460,21 @@ int lowm_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K,
                      void* workspace, void* stream) {
   return lowm::launch(A, W, C, false, M, N, K, split_k, workspace,
                       static_cast<hipStream_t>(stream), nullptr);
+}
+
+int lowm_gemm_splitk_noalloc(const void* A, const void* W, void* C, int M, int N, int K,
+                             int split_k, void* stream) {
+  int rc = lowm::check_sizes(M, N, K, split_k);
+  if (rc != LOWM_OK) return rc;
+  if (!A || !W || !C) return LOWM_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (split_k > 1) {
+    if (lowm::workspace_bytes(M, N, K, split_k) > lowm::kScratchBytes) return LOWM_ERR_SCRATCH;
+    rc = lowm::scratch_address(static_cast<hipStream_t>(stream), &ws);
+    if (rc != LOWM_OK) return rc;
+  }
+  return lowm::launch(A, W, C, false, M, N, K, split_k, ws, static_cast<hipStream_t>(stream),
+                      nullptr);
 }
 
 int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C, int M, int N, int K,
@@ -494,6 +566,9 @@ const char* lowm_strerror(int code) {
              "pointer, or tactic not in this build)";
     case LOWM_ERR_WORKSPACE: return "split_k > 1 needs a workspace";
     case LOWM_ERR_LAUNCH: return "kernel launch failed (see lowm_last_hip_error)";
+    case LOWM_ERR_SCRATCH:
+      return "the sizes need more workspace than the built-in scratch of "
+             "lowm_gemm_splitk_noalloc (LOWM_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }

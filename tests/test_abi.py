@@ -331,3 +331,18 @@ def test_push_wait_validation(lib):
     assert w(FLAG_ADDR, 4, 1, 10_000_001, FAKE, None) == E.LOWM_ERR_UNSUPPORTED
     assert w(FLAG_ADDR + 2, 4, 1, 10, FAKE, None) == E.LOWM_ERR_UNSUPPORTED
     assert lib.lib.lowm_last_hip_error() == 0
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """Before any HIP call: a workspace larger than the built-in scratch is
+    LOWM_ERR_SCRATCH; argument errors are those of lowm_gemm_splitk."""
+    fn = lib.lib.lowm_gemm_splitk_noalloc
+    M, N, K, S = 64, 16384, 4096, 8
+    assert lib.workspace_bytes(M, N, K, S) > binding.SCRATCH_BYTES
+    assert fn(FAKE, FAKE, FAKE, M, N, K, S, None) == binding.LOWM_ERR_SCRATCH
+    assert "scratch" in lib.strerror(binding.LOWM_ERR_SCRATCH)
+    assert fn(None, FAKE, FAKE, 4, 64, 256, 2, None) == binding.LOWM_ERR_INVALID_ARG
+    assert fn(FAKE, FAKE, FAKE, 65, 64, 256, 2, None) == binding.LOWM_ERR_UNSUPPORTED
+    assert fn(FAKE, FAKE, FAKE, 4, 64, 260, 2, None) == binding.LOWM_ERR_UNSUPPORTED
+    # the largest sweep shape fits
+    assert lib.workspace_bytes(64, 6144, 4096, 8) <= binding.SCRATCH_BYTES
