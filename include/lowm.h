@@ -80,7 +80,10 @@ extern "C" {
 
 /*
  * C (bf16 [M, N]) = A (bf16 [M, K]) * W (bf16 [N, K])^T, fp32 accumulation,
- * split_k equal K slices folded in rank order by the last-arriving rank.
+ * split_k equal K slices folded in rank order by the last-arriving rank
+ * (PR "Fix two synchronization gaps in the MiniMax M3 low-M split-K GEMM",
+ * Description item 2: each rank's fp32 partial over its part of K, summed
+ * by one owner; Hardware verification: bf16 operands and output).
  * `workspace` may be NULL when split_k == 1.  `stream` is a hipStream_t.
  */
 int lowm_gemm_splitk(const void* A, const void* W, void* C,
@@ -90,7 +93,11 @@ int lowm_gemm_splitk(const void* A, const void* W, void* C,
 /*
  * The same product with an fp32 result: C is float [M, N].  Same kernel and
  * summation order; only the final store differs, so the bf16 entry point's
- * output is exactly this result rounded to nearest-even.
+ * output is exactly this result rounded to nearest-even.  The fp32 sum is
+ * what the pages check against: the PR's Hardware verification compares
+ * each output with the fp32 product of the same operands, and the integer
+ * closed form of the Triton issue "warpgroup_mma_wait does not properly
+ * synchronize across warpgroups" (Describe the bug) is exact only in fp32.
  */
 int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C,
                             int M, int N, int K, int split_k,
@@ -99,13 +106,20 @@ int lowm_gemm_splitk_f32out(const void* A, const void* W, float* C,
 /*
  * Bytes of workspace a launch with these sizes needs: 0 when split_k == 1,
  * else the counters (256 bytes per 16 columns of C) plus the fp32 partials,
- * split_k * M * round_up(N, 64) floats.  Returns
- * 0 as well for arguments the launch would reject.
+ * split_k * M * round_up(N, 64) floats.  Returns 0 as well for arguments the
+ * launch would reject.  The workspace carries the split-K exchange that the
+ * PR's Description item 2 runs through a shared-memory mailbox inside a
+ * 2-CTA cluster; gfx950 has neither, so the partials and the arrival counts
+ * go through device memory instead.  Host-only; no HIP call.
  */
 size_t lowm_gemm_splitk_workspace_bytes(int M, int N, int K, int split_k);
 
 /*
- * Batched launch: `count` (1 .. LOWM_MAX_BATCH) independent products
+ * Batched launch (the pages' kernel runs with programmatic dependent launch,
+ * which lets the next kernel start while this one is in its main loop: PR,
+ * Description item 1 and Hardware verification; ROCm has no such launch, and
+ * this entry point hides the same launch gaps by running several GEMMs of
+ * one layer in one launch): `count` (1 .. LOWM_MAX_BATCH) independent products
  * C_g = A_g * W_g^T that share M, K, split_k and the bf16 output, in one
  * kernel launch (one launch gap instead of `count`; the GEMMs' tails
  * overlap).  Each GEMM is exactly what lowm_gemm_splitk computes for it: one
@@ -135,11 +149,13 @@ int lowm_gemm_splitk_batched(const lowm_gemm_desc* gemms, int count, int M, int 
 size_t lowm_gemm_splitk_batched_workspace_bytes(const lowm_gemm_desc* gemms, int count,
                                                 int M, int K, int split_k);
 
-/* Static text naming an error code. */
+/* Static text naming an error code.  (Error reporting of the host launch
+ * path; the PR's Description item 1 has the host guarantee a non-empty K
+ * loop, which this library checks and reports as LOWM_ERR_UNSUPPORTED.) */
 const char* lowm_strerror(int code);
 
 /* hipError_t of the most recent failed launch on the calling thread (0 if
- * none). */
+ * none); the cause behind LOWM_ERR_LAUNCH. */
 int lowm_last_hip_error(void);
 
 /*
@@ -196,24 +212,30 @@ typedef struct lowm_tactic {
 } lowm_tactic;
 
 /* The tactic lowm_gemm_splitk would use for these sizes (written to *out).
- * Returns LOWM_OK or an error code for sizes it would reject. */
+ * Returns LOWM_OK or an error code for sizes it would reject.  Host-only.
+ * (The PR ships one fixed tactic per split_k, Hardware verification; this
+ * one is chosen per shape from measurements on MI355X.) */
 int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out);
 
 /* Host-only: a split_k for these sizes (written to *split_k), chosen from a
- * table of the fastest split_k measured on MI355X over M 4 and 16, N 768 ..
- * 24576, K 2048 .. 16384 (nearest grid point in log2 N and log2 K; M <= 8
- * uses the M 4 measurements), reduced to a power of two that K allows.  Any
- * split_k is correct; this one minimises time per call.  Returns LOWM_OK, or
- * the error code a launch would return for M, N, K. */
+ * table of the fastest split_k measured on MI355X (bench.py --split-sweep)
+ * over M 4 and 16, N 768 .. 24576, K 2048 .. 16384 (nearest grid point in
+ * log2 N and log2 K; M <= 8 uses the M 4 measurements), reduced to a power
+ * of two that K allows.  Any split_k is correct; this one minimises time per
+ * call.  (The PR ships split_k 1 and 2, Hardware verification.)  Returns
+ * LOWM_OK, or the error code a launch would return for M, N, K. */
 int lowm_pick_split_k(int M, int N, int K, int* split_k);
 
 /* Host-only: LOWM_OK if a launch with these sizes, output type (f32out != 0:
  * fp32) and tactic (NULL: the default) would find a kernel in this build, else
- * the error code the launch would return for them.  No HIP call is made. */
+ * the error code the launch would return for them (the host-side checks of
+ * lowm_gemm_splitk, including the PR's non-empty K loop of Description
+ * item 1).  No HIP call is made. */
 int lowm_check_launch(int M, int N, int K, int split_k, int f32out,
                       const lowm_tactic* tactic);
 
-/* lowm_gemm_splitk / _f32out with an explicit tactic (NULL: the default).
+/* lowm_gemm_splitk / _f32out with an explicit tactic (NULL: the default),
+ * the same product (PR, Description item 2) in another summation order.
  * LOWM_ERR_UNSUPPORTED for a tactic this build does not provide. */
 int lowm_gemm_splitk_ex(const void* A, const void* W, void* C,
                         int M, int N, int K, int split_k,
@@ -258,13 +280,16 @@ int lowm_gemm_splitk_push(const void* A, const void* W, void* C, int M, int N, i
                           const lowm_tactic* tactic);
 
 /*
- * Consumer side of the push epilogue: enqueues on `stream` one wavefront that
- * polls flags[0 .. n_flags-1] with system-scope loads until each equals
- * flag_value, or until timeout_us microseconds have passed, and then writes
- * to the device int *missing the number of flags it did not see set (0: all
- * were).  Work enqueued after it on `stream` runs after it.  n_flags 1 ..
- * 4096, timeout_us <= 10,000,000, flag_value non-zero; the wait is bounded
- * whether or not any producer runs.
+ * Consumer side of the push epilogue (the publication the PR's Hardware
+ * verification and Test Coverage name, read as above): enqueues on `stream`
+ * one wavefront that polls flags[0 .. n_flags-1] with system-scope loads
+ * until each equals flag_value, or until timeout_us microseconds have
+ * passed, and then writes to the device int *missing the number of flags it
+ * did not see set (0: all were).  Work enqueued after it on `stream` runs
+ * after it.  `flags` must hold at least n_flags words (the library cannot
+ * check this: a shorter buffer is read past its end); n_flags 1 .. 4096,
+ * timeout_us <= 10,000,000, flag_value non-zero; the wait is bounded whether
+ * or not any producer runs.
  */
 int lowm_push_wait(const uint32_t* flags, int n_flags, uint32_t flag_value,
                    uint32_t timeout_us, int* missing, void* stream);

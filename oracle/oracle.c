@@ -131,11 +131,3 @@ void oracle_gemm_f64_cols(const uint16_t* A, const uint16_t* W,
     free(a);
     free(w);
 }
-
-/* The whole product: all N columns. */
-void oracle_gemm_f64(const uint16_t* A, const uint16_t* W,
-                     int64_t M, int64_t N, int64_t K,
-                     double* C, double* S)
-{
-    oracle_gemm_f64_cols(A, W, M, N, K, 0, N, C, S);
-}

@@ -224,6 +224,8 @@ class Library:
         if split_k <= 1:
             return 0
         need = self.workspace_bytes(M, N, K, split_k)
+        if need == 0:   # sizes the launch rejects: report its error code
+            self.check(self.check_launch(M, N, K, split_k))
         if workspace is None:
             raise ValueError(f"split_k={split_k} needs a zeroed workspace of {need} bytes "
                              "(make_workspace)")
@@ -259,6 +261,9 @@ class Library:
         of flags not seen set lands in missing[0] (an int32 GPU tensor)."""
         if missing.dtype != torch.int32 or not missing.is_cuda or flags.dtype != torch.int32:
             raise ValueError("flags and missing must be int32 GPU tensors")
+        if not flags.is_cuda or not flags.is_contiguous() or not 1 <= n_flags <= flags.numel():
+            raise ValueError(f"flags must be a contiguous GPU tensor of at least n_flags = "
+                             f"{n_flags} (>= 1) words")
         s = stream if stream is not None else torch.cuda.current_stream(flags.device)
         self.check(self.lib.lowm_push_wait(flags.data_ptr(), n_flags, flag_value, timeout_us,
                                            missing.data_ptr(), s.cuda_stream))

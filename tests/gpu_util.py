@@ -13,6 +13,16 @@ import workloads
 from split_bf16_gemm_amd import binding
 
 
+# Every bf16 output judged against the oracle: (case, elements, n_cancel,
+# max_ulp), where n_cancel counts the elements that passed only through the
+# cancellation rule of tests/checks.py.  Printed at the end of the session.
+CANCEL_REPORT: list = []
+
+
+def report(what: str, v: dict, elements: int):
+    CANCEL_REPORT.append((what, elements, v["n_cancel"], v["max_ulp"]))
+
+
 def say(*parts):
     """Name the case before a GPU step, flushed, so a fault can be placed."""
     print("[gpu]", *parts, file=sys.stderr, flush=True)
@@ -94,4 +104,6 @@ def assert_bf16_launch(lib, A_dev, W_dev, wl, bits, tactic=None, what=""):
     assert_fp32(c32, C, S, what=what)
     assert np.array_equal(bits, oracle.round_bf16(c32.astype(np.float64))), \
         f"{what}: bf16 output is not RNE of the fp32 sibling"
-    return assert_bf16(bits, C, S, wl.K, oracle.default(), c32, what=what)
+    v = assert_bf16(bits, C, S, wl.K, oracle.default(), c32, what=what)
+    report(what or wl.name, v, C.size)
+    return v

@@ -19,7 +19,7 @@ import oracle
 import split_bf16_gemm_amd as sbg
 import workloads
 from checks import assert_bf16, assert_exact_integer, assert_fp32
-from gpu_util import all_tactics, device, inputs, oracle_result, run, say, to_bits
+from gpu_util import all_tactics, device, inputs, oracle_result, report, run, say, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,7 @@ def check_random(lib, wl, tactic=None, what=""):
     v = assert_bf16(b16, C, S, wl.K, oracle.default(), c32, what=what or wl.name)
     # the two entry points share the kernel and its order: bf16 = RNE(fp32)
     assert np.array_equal(b16, oracle.round_bf16(c32.astype(np.float64))), what
+    report(what or wl.name, v, C.size)
     return v
 
 
@@ -115,18 +116,31 @@ def test_ragged(lib, M, N, K, S):
 
 
 def test_every_tactic_random(lib):
+    """M 20 (two row blocks) with whole 256-K slices: every tactic family
+    applies (5 register/LDS variants at 16 rows, 4 at 32, 3 line-pair rings,
+    3 panel rings)."""
     wl = workloads.Workload("tactics", 20, 300, 2048, 2, seed_a=77, seed_w=78)
-    ran = 0
+    ran = []
     for t in all_tactics(wl.M):
         if check_random(lib, wl, tactic=t, what=repr(t)) is not None:
-            ran += 1
-    assert ran >= 7
+            ran.append(t)
+    assert len(ran) == 15, ran
 
 
 def test_every_tactic_small_m_ragged_k(lib):
+    """K / split_k = 344 is neither whole line pairs per wavefront nor whole
+    64-K steps, and M 4 is one row block: the register rings of 4 and 8
+    chunks and both LDS rings run at 16 and 32 rows (8 tactics); the
+    line-pair and panel tiles, and the 16-chunk register ring (too many
+    registers), return LOWM_ERR_UNSUPPORTED."""
     wl = workloads.Workload("tactics_k", 4, 97, 1032, 3, seed_a=5, seed_w=6)
+    ran = []
     for t in all_tactics(wl.M):
-        check_random(lib, wl, tactic=t, what=repr(t))
+        if check_random(lib, wl, tactic=t, what=repr(t)) is not None:
+            ran.append(t)
+    stages = sorted({t.stage for t in ran})
+    assert stages == [sbg.binding.LOWM_STAGE_LDS, sbg.binding.LOWM_STAGE_REG], ran
+    assert len(ran) == 8, ran
 
 
 def test_workspace_returns_to_zero_and_guard_intact(lib):

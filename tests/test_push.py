@@ -1,12 +1,14 @@
 """Push epilogue: each output tile's owner also writes the bf16 tile into a
 caller-given exchange buffer and then sets one flag per 16 output columns.
 
-Checked here: the pushed copy is bit-identical to C (which is itself the
-plain launch's output), it lands exactly in the [M, N] window of a wider
+Checked here: C and the pushed copy are each judged against the fp64 oracle
+(the bars of tests/checks.py) and are bit-identical to each other and to the
+plain launch's output; the copy lands exactly in the [M, N] window of a wider
 strided buffer and nowhere else, each flag of the GEMM holds the caller's
 value and the flags after them are untouched; a consumer that waits for the
 flags on a second stream while the GEMM runs sees every flag and the final
-values; the wait gives up, bounded, on flags that no launch sets."""
+values, which are judged against the oracle too; the wait gives up, bounded,
+on flags that no launch sets."""
 from __future__ import annotations
 
 import numpy as np
@@ -15,7 +17,7 @@ import torch
 
 import split_bf16_gemm_amd as sbg
 import workloads
-from gpu_util import device, inputs, say, to_bits
+from gpu_util import assert_bf16_launch, device, inputs, say, to_bits
 from split_bf16_gemm_amd import binding
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +32,11 @@ CASES = [  # M, N, K, split_k
     (1, 2304, 12288, 4),
 ]
 
-TACTICS = [None, ("reg", 16, 4, 2), ("panel", 64, 2, 4), ("lds", 16, 4, 2), ("reg", 32, 4, 2)]
+TACTICS = [None, ("reg", 16, 4, 2), ("lds", 16, 4, 2), ("reg", 32, 4, 2)]
+# panel tiles exist for 17..64 activation rows only
+PANEL_CASES = [(20, 520, 2048, 2), (64, 1000, 4096, 4), (33, 6144, 4096, 1)]
+PAIRS = ([(c, t) for c in CASES for t in TACTICS] +
+         [(c, ("panel", 64, 2, 4)) for c in PANEL_CASES])
 
 
 def window(M, N, dev, off=24, extra=40):
@@ -39,9 +45,11 @@ def window(M, N, dev, off=24, extra=40):
     return big, big[:, off:off + N], off
 
 
-@pytest.mark.parametrize("M,N,K,S", CASES)
-@pytest.mark.parametrize("tac", TACTICS, ids=lambda t: "default" if t is None else ":".join(map(str, t)))
-def test_push_copy_window_and_flags(M, N, K, S, tac):
+@pytest.mark.parametrize("case,tac", PAIRS, ids=lambda x: (
+    "x".join(map(str, x)) if isinstance(x, tuple) and isinstance(x[0], int)
+    else "default" if x is None else ":".join(map(str, x))))
+def test_push_copy_window_and_flags(case, tac):
+    M, N, K, S = case
     lib = sbg.load()
     dev = device()
     wl = workloads.Workload(f"push_m{M}_n{N}_k{K}_s{S}", M, N, K, S, seed_a=31, seed_w=32)
@@ -53,12 +61,7 @@ def test_push_copy_window_and_flags(M, N, K, S, tac):
     big, win, off = window(M, N, dev)
     ws = lib.make_workspace(M, N, K, S, dev)
     say("push", M, N, K, S, tac)
-    try:
-        C = lib.gemm_push(A, W, S, win, flags, 7, workspace=ws, tactic=tactic)
-    except sbg.LowmError as e:
-        if tactic is not None and e.code == binding.LOWM_ERR_UNSUPPORTED:
-            pytest.skip(f"tactic {tac} is not built for M {M}")
-        raise
+    C = lib.gemm_push(A, W, S, win, flags, 7, workspace=ws, tactic=tactic)
     torch.cuda.synchronize()
     plain = lib.gemm(A, W, S, workspace=ws, tactic=tactic)
     torch.cuda.synchronize()
@@ -66,6 +69,10 @@ def test_push_copy_window_and_flags(M, N, K, S, tac):
     assert np.array_equal(c, to_bits(plain)), "C of the push launch differs from the plain launch"
     b = to_bits(big)
     assert np.array_equal(b[:, off:off + N], c), "pushed copy differs from C"
+    what = f"push {M}x{N}x{K} s{S} {tac}"
+    assert_bf16_launch(lib, A, W, wl, c, tactic=tactic, what=what + ": C")
+    assert_bf16_launch(lib, A, W, wl, np.ascontiguousarray(b[:, off:off + N]), tactic=tactic,
+                       what=what + ": pushed copy")
     outside = np.ones(b.shape, dtype=bool)
     outside[:, off:off + N] = False
     assert (b[outside] == 0xFFFF).all(), "the push wrote outside its [M, N] window"
@@ -101,6 +108,7 @@ def test_push_consumer_waits_on_another_stream():
     torch.cuda.synchronize()
     assert int(missing.item()) == 0, f"the consumer timed out with {int(missing.item())} flags unseen"
     assert np.array_equal(to_bits(got), to_bits(C)), "the consumer read values before the final ones"
+    assert_bf16_launch(lib, A, W, wl, to_bits(got), what="push consumer's copy")
 
 
 def test_push_wait_times_out_on_flags_never_set():
@@ -113,6 +121,11 @@ def test_push_wait_times_out_on_flags_never_set():
     lib.push_wait(flags, 100, 5, 2000, missing)
     torch.cuda.synchronize()
     assert int(missing.item()) == 100 - 34
+    # more flags than the tensor holds: refused before any launch
+    with pytest.raises(ValueError):
+        lib.push_wait(flags, 101, 5, 2000, missing)
+    with pytest.raises(ValueError):
+        lib.push_wait(flags[::2], 10, 5, 2000, missing)
 
 
 def test_push_flag_value_per_call():
@@ -135,3 +148,4 @@ def test_push_flag_value_per_call():
         assert int(missing.item()) == 0
         assert (flags.cpu().numpy() == value).all()
         assert np.array_equal(to_bits(dst), to_bits(C))
+        assert_bf16_launch(lib, A, W, wl, to_bits(dst), what=f"push value {value}")
