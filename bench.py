@@ -343,27 +343,176 @@ def counter_summary(dirs, kernel_filter="lowm_"):
             print(f"| {c} | {statistics.median(v):,.0f} | {len(v)} |")
 
 
-def cpu_baseline(wl, budget_s=10.0):
-    """The fp64 oracle on the host cores: full products of the workload,
-    repeated until about budget_s seconds of CPU work."""
+def trace_breakdown(dev, wl, tactic, launches=4):
+    """Where a launch's time goes, from the stress build's per-workgroup
+    timestamps (s_memrealtime, 100 MHz): dispatch (first entry to this
+    workgroup's entry), first data (entry to its first stage or line pair in
+    LDS), stream (to the end of its main loop), reduction (wavefront sums
+    through LDS), tail (publish / exchange / fold / store, to its end).
+    Medians over all workgroups and over the last 5 % to end, per traced
+    launch; traced launches alternate with untraced ones through the same
+    rotated pool.  The timestamp stores share the vector-memory counter with
+    the loads, so the traced kernel waits a little more than the product
+    kernel: a picture of the timeline, not a timing."""
+    import numpy as np
+    import torch
+    import split_bf16_gemm_amd as sbg
+    stress = sbg.load("stress")
+    M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
+    tac = tactic if tactic is not None else stress.pick_tactic(M, N, K, S)
+    tiles = -(-N // tac.rows)
+    grid = (tiles + 7) // 8 * 8 * S
+    T = stress.TRACE_SLOTS
+    per_set = 2 * K * N + 2 * M * K + 2 * M * N + stress.workspace_bytes(M, N, K, S)
+    sets = max(2, math.ceil(2 * MALL_BYTES / per_set) + 1)
+    pool = Pool(stress, wl, sets, dev)
+    call = make_caller(stress, wl, tactic, torch.cuda.current_stream(dev).cuda_stream)
+    for i in range(2 * sets):
+        call(pool.ptrs[i % sets])
+    torch.cuda.synchronize()
+    buf = torch.zeros(grid * T, dtype=torch.int64, device=dev)
+    print(f"{wl.name}, tactic {tactic_text(tac)}, {grid} workgroups ({tiles} tiles x "
+          f"split_k {S}); microseconds from the first workgroup's entry")
+    print("| launch | span | WGs | dispatch | first data | stream | reduction | tail | "
+          "last 5 %: dispatch | first data | stream | reduction | tail | end | early owners |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    ends = []
+    for it in range(launches):
+        buf.zero_()
+        torch.cuda.synchronize()
+        stress.trace(buf)
+        try:
+            call(pool.ptrs[it % sets])
+            torch.cuda.synchronize()
+        finally:
+            stress.trace(None)
+        call(pool.ptrs[(it + 1) % sets])
+        torch.cuda.synchronize()
+        tr = buf.view(grid, T).cpu().numpy().astype(np.int64)
+        valid = (tr[:, 8] < tiles) & (tr[:, 5] > 0)
+        t = tr[valid]
+        t0 = t[:, 0].min()
+        us = (t[:, :6] - t0) / 100.0
+        entry, first, lend, red, arr, end = (us[:, c] for c in range(6))
+        red = np.where(t[:, 3] > 0, red, lend)
+        segs = [entry, first - entry, lend - first, red - lend, end - red]
+        last = end >= np.percentile(end, 95)
+        early = int(((t[:, 4] == 0) & (t[:, 9] == S - 1)).sum()) if S > 1 else 0
+        cells = [f"{np.median(x):.2f}" for x in segs] + \
+                [f"{np.median(x[last]):.2f}" for x in segs] + [f"{np.median(end[last]):.2f}"]
+        print(f"| {it} | {end.max():.2f} | {int(valid.sum())} | " + " | ".join(cells) +
+              f" | {early} |", flush=True)
+        ends.append((end, t[:, 9], t[:, 7], first))
+    # per rank and per XCD: when workgroups end, and when their first data came
+    end = np.concatenate([e[0] for e in ends])
+    rank = np.concatenate([e[1] for e in ends])
+    xcd = np.concatenate([e[2] for e in ends])
+    first = np.concatenate([e[3] for e in ends])
+    print()
+    print("| group | WGs | first data median / p95 | end median / p95 / max |")
+    print("|---|---|---|---|")
+    for label, key, values in (("rank", rank, range(S)), ("XCD", xcd, sorted(set(xcd.tolist())))):
+        for v in values:
+            sel = key == v
+            if sel.any():
+                print(f"| {label} {v} | {int(sel.sum()) // launches} | "
+                      f"{np.median(first[sel]):.2f} / {np.percentile(first[sel], 95):.2f} | "
+                      f"{np.median(end[sel]):.2f} / {np.percentile(end[sel], 95):.2f} / "
+                      f"{end[sel].max():.2f} |")
+
+
+def host_threads() -> int:
+    """Worker threads for the oracle: the CPUs this process may run on, at
+    most 16 (one GPU's share of the box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_product(orc, a, w, threads: int):
+    """The whole product C = A W^T from the oracle's column-range entry,
+    split over `threads` Python threads by columns (each ctypes call releases
+    the GIL, so the ranges run in parallel; the arithmetic per column is the
+    oracle's own)."""
+    from concurrent.futures import ThreadPoolExecutor
+    N = w.shape[0]
+    if threads == 1:
+        return orc.gemm_cols(a, w, 0, N)
+    bounds = [N * i // threads for i in range(threads + 1)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        parts = list(ex.map(lambda i: orc.gemm_cols(a, w, bounds[i], bounds[i + 1]),
+                            range(threads)))
+    import numpy as np
+    return np.concatenate([c for c, _ in parts], axis=1), np.concatenate([s for _, s in parts],
+                                                                         axis=1)
+
+
+def time_oracle(wl, threads: int, min_runs: int = 3, budget_s: float = 5.0):
+    """Median ms per whole product of the fp64 oracle on `threads` host
+    threads: at least min_runs products, more while within budget_s."""
     import oracle
     import workloads
     A, W = workloads.make_inputs(wl)
     a, w = workloads.bits(A), workloads.bits(W)
     orc = oracle.default()
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        orc.gemm(a, w)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < min_runs or time.perf_counter() - t_start < budget_s:
+        t0 = time.perf_counter()
+        oracle_product(orc, a, w, threads)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 50:
             break
-    dt = (time.perf_counter() - t0) / n
+    return statistics.median(times) * 1e3, len(times)
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle on the host cores, for the benchmark's JSON line: whole
+    products of the workload, on one thread and on T threads (columns split
+    between them), median of at least 3 each, about 10 s of CPU time in all.
+    `value` is the T-thread rate in the metric's unit."""
+    T = host_threads()
+    ms1, n1 = time_oracle(wl, 1)
+    msT, nT = time_oracle(wl, T)
     b = algorithmic_bytes(wl.M, wl.N, wl.K, wl.split_k)
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full {wl.name} products (fp64, single thread), "
-                      f"{dt * 1e3:.1f} ms each",
-            "ms_per_call": round(dt * 1e3, 2)}
+    return {"value": round(b / (msT * 1e-3) / 1e9, 4), "unit": "GB/s", "cores": T,
+            "kind": "oracle",
+            "sample": f"whole {wl.name} products (fp64, columns split over {T} threads): "
+                      f"median of {nT}; single thread: median of {n1}",
+            "ms_per_call": round(msT, 2), "ms_per_call_1_thread": round(ms1, 2),
+            "value_1_thread": round(b / (ms1 * 1e-3) / 1e9, 4),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_table():
+    """Markdown table: the fp64 oracle's ms per whole product, 1 thread and
+    T threads, for the pages' shapes and the ends of the M sweep (the oracle
+    does not depend on split_k)."""
+    import workloads
+    T = host_threads()
+    model = cpu_model()
+    names = ["int_closed_form_m4_n512_k1024_s2", "m4_n6144_k4096_s2", "m4_n2304_k12288_s4",
+             "m4_n49152_k4096_s2", "sweep_m1_n6144_k4096_s1", "sweep_m64_n6144_k4096_s1"]
+    print(f"host: {os.cpu_count()} CPUs visible, {T} used; {model}")
+    print("| workload | oracle ms, 1 thread | oracle ms, T threads | T | CPU model |")
+    print("|---|---|---|---|---|")
+    for name in names:
+        wl = workloads.by_name(name)
+        ms1, _ = time_oracle(wl, 1, budget_s=0)
+        msT, _ = time_oracle(wl, T, budget_s=0)
+        print(f"| {name} | {ms1:.1f} | {msT:.1f} | {T} | {model} |", flush=True)
 
 
 def config_table(lib, dev, steps, reps):
@@ -506,6 +655,12 @@ def main():
     ap.add_argument("--split-sweep", metavar="MS",
                     help="comma-separated M values: time split_k 1/2/4/8 with the default "
                          "tactic over the N x K grid and print the fastest per shape")
+    ap.add_argument("--trace", action="store_true",
+                    help="timeline of --workload (and --tactic) from the stress build's "
+                         "per-workgroup timestamps; print a markdown table")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="no GPU: time the fp64 oracle (1 and T threads) on the pages' "
+                         "shapes and the M-sweep ends; print a markdown table")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy kernel (50,331,648 bytes per launch) so "
                          "profiler byte counters can be scaled against a known size")
@@ -518,6 +673,9 @@ def main():
 
     if args.counter_summary:
         counter_summary(args.counter_summary)
+        return
+    if args.cpu_table:
+        cpu_table()
         return
 
     if args.gpus != 1:
@@ -539,6 +697,9 @@ def main():
     lib = sbg.load()
     if args.table:
         config_table(lib, dev, args.steps, args.reps)
+        return
+    if args.trace:
+        trace_breakdown(dev, workloads.by_name(args.workload), parse_tactic(args.tactic))
         return
     if args.tactic_matrix:
         names, tacs = (x.split(",") for x in args.tactic_matrix)

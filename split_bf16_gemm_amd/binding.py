@@ -320,9 +320,11 @@ class Library:
             return None
         return torch.zeros(n, dtype=torch.uint8, device=device)
 
+    TRACE_SLOTS = 10    # entry, first stage, loop end, reduced, arrived, end, CU, XCD, tile, rank
+
     def trace(self, buf: Optional[torch.Tensor]):
         """Stress build: per-workgroup timestamps into ``buf`` (int64 device
-        tensor, 8 per workgroup), or stop tracing with None."""
+        tensor, TRACE_SLOTS per workgroup), or stop tracing with None."""
         if not self.has_stress:
             raise RuntimeError(f"{self.path.name} is not a stress build")
         self.check(self.lib.lowm_stress_trace(None if buf is None else buf.data_ptr()))

@@ -591,8 +591,10 @@ int lowm_stress_configure(unsigned site_mask, int rank, int wave, int tile_mod, 
   return LOWM_OK;
 }
 
-// Stress build only: record per-workgroup timestamps into `buf` (device
-// memory, 8 uint64 per workgroup of the grid; NULL stops tracing).
+// Stress build only: record per-workgroup timestamps and ids into `buf`
+// (device memory, 10 uint64 per workgroup of the grid: entry, first stage,
+// loop end, reduced, arrived, end, CU id, XCD id, tile, rank; NULL stops
+// tracing).
 int lowm_stress_trace(void* buf) {
   lowm::g_stress.trace = static_cast<uint64_t*>(buf);
   return LOWM_OK;

@@ -52,13 +52,15 @@ struct StressArgs {
 };
 
 // Timestamp trace of the stress build: per workgroup, s_memrealtime (100 MHz)
-// at these points, then the hardware ids of the CU and XCD it ran on.  The
+// at these points, then the hardware ids of the CU and XCD it ran on and the
+// (tile, rank) it worked on (kTraceSlots 64-bit words per workgroup).  The
 // timestamps are global stores, counted by the same vector-memory counter as
 // the loads whose completion the explicit s_waitcnt of the LDS-ring variants
 // assumes: a traced launch measures timing only, its output is not checked.
 enum TraceSlot : int {
   kTraceEntry = 0, kTraceFirstStage = 1, kTraceLoopEnd = 2, kTraceReduced = 3,
-  kTraceArrived = 4, kTraceEnd = 5, kTraceHwId = 6, kTraceXccId = 7, kTraceSlots = 8
+  kTraceArrived = 4, kTraceEnd = 5, kTraceHwId = 6, kTraceXccId = 7, kTraceTile = 8,
+  kTraceRank = 9, kTraceSlots = 10
 };
 
 struct Args {

@@ -130,14 +130,15 @@ def _early_owners(stress, ops, wl):
     A, W, ws = ops
     tiles = (wl.N + 15) // 16
     grid = (tiles + 7) // 8 * 8 * wl.split_k
-    buf = torch.zeros(grid * 8, dtype=torch.int64, device=A.device)
+    T = stress.TRACE_SLOTS
+    buf = torch.zeros(grid * T, dtype=torch.int64, device=A.device)
     stress.trace(buf)
     try:
         stress.gemm(A, W, wl.split_k, workspace=ws)
         torch.cuda.synchronize()
     finally:
         stress.trace(None)
-    tr = buf.view(grid, 8).cpu().numpy()
+    tr = buf.view(grid, T).cpu().numpy()
     return int(((tr[:, 5] > 0) & (tr[:, 4] == 0)).sum())
 
 
