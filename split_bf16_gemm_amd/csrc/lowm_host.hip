@@ -111,8 +111,15 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
   // step shared in LDS by the four wavefronts), ring of 4 steps.  Measured on
   // MI355X at M 32 and M 64, N 6144, K 4096, split_k 1..8: 1.3-2.1x faster
   // than the line-pair and register tiles at every point; rings of 3 and 6
-  // are within a few percent, 3 slower at M 64.
+  // are within a few percent, 3 slower at M 64.  Where 64-row tiles would
+  // give fewer than 192 workgroups (CUs left idle), 32-row tiles whose two
+  // wavefront pairs split the K slice in halves: M 32 / M 64 at split_k 1,
+  // N 6144: 13.6 / 17.2 us against 18.9 / 21.9 with 64-row tiles; with 192
+  // or more workgroups they lose (split_k 2: 15.7 / 21.3 against 15.1 / 18.5).
   if (M > 16 && nvec % 8 == 0) {
+    const long tiles64 = (N + 63) / 64;
+    t->rows = (tiles64 * S < 192 && nvec % 16 == 0) ? 32 : 64;
+    if (provides({kStagePanel, 2, 4})) return LOWM_OK;
     t->rows = 64;
     if (provides({kStagePanel, 2, 4})) return LOWM_OK;
   }
@@ -140,28 +147,45 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
   return LOWM_ERR_UNSUPPORTED;
 }
 
-// split_k for a shape, from a table of the fastest measured on MI355X (default
-// tactic for each split_k, W streamed from HBM): M 4 and 16, N 768 .. 24576,
-// K 2048 .. 16384, split_k 1, 2, 4, 8.  A shape takes its nearest grid point
-// in log2 N and log2 K; M <= 8 uses the M 4 row, larger M the M 16 row.  On
-// the grid every entry is the fastest split_k; off it, the neighbours were
-// within 10 % of each other's best.  split_k pays when the tiles are few and
-// K is long; for M 16 the larger partials make it pay less often.
-constexpr unsigned char kBestSplit[2][6][4] = {
+// split_k for a shape, from a table of the fastest measured on MI355X
+// (bench.py --split-sweep: the default tactic for each split_k, W streamed
+// from HBM through a rotated pool, median of 3 x 40 calls): M 4, 16, 32 and
+// 64, N 768 .. 24576, K 2048 .. 16384, split_k 1, 2, 4, 8.  A shape takes its
+// nearest grid point in log2 N and log2 K and the row of the next measured M
+// at or above its own.  On the grid every entry is the fastest split_k; some
+// neighbours are within a few percent of each other.  split_k pays when the
+// tiles are few and K is long; the larger the partials (M), the less often.
+constexpr int kSplitRows = 4;
+constexpr int kSplitRowM[kSplitRows] = {8, 16, 32, 64};   // M 4 measured for M <= 8
+constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
     // M <= 8            K: 2048 4096 8192 16384
-    {{1, 4, 4, 8},    // N 768
-     {2, 2, 4, 4},    // N 1536
+    {{4, 4, 4, 8},    // N 768
+     {4, 2, 4, 4},    // N 1536
      {1, 2, 2, 4},    // N 3072
      {1, 2, 2, 8},    // N 6144
      {1, 1, 2, 8},    // N 12288
      {1, 1, 2, 8}},   // N 24576
-    // M > 8
+    // 8 < M <= 16
     {{1, 4, 4, 4},
-     {1, 2, 8, 8},
+     {1, 4, 8, 8},
      {1, 1, 4, 4},
-     {1, 1, 2, 4},
+     {1, 1, 2, 2},
      {1, 1, 1, 1},
-     {1, 1, 1, 1}}};
+     {1, 1, 1, 1}},
+    // 16 < M <= 32
+    {{4, 4, 8, 8},
+     {4, 4, 4, 4},
+     {2, 2, 2, 4},
+     {1, 1, 1, 2},
+     {1, 1, 1, 4},
+     {1, 1, 2, 2}},
+    // 32 < M <= 64
+    {{4, 4, 8, 8},
+     {1, 4, 4, 4},
+     {1, 4, 4, 4},
+     {1, 1, 1, 2},
+     {1, 1, 1, 1},
+     {1, 1, 1, 2}}};
 
 int nearest_log2_index(double x, double base, int last) {
   const int i = (int)floor(log2(x / base) + 0.5);
@@ -172,8 +196,9 @@ int pick_split(int M, int N, int K, int* split_k) {
   if (!split_k) return LOWM_ERR_INVALID_ARG;
   int rc = check_sizes(M, N, K, 1);
   if (rc != LOWM_OK) return rc;
-  int S = kBestSplit[M <= 8 ? 0 : 1][nearest_log2_index(N, 768.0, 5)]
-                    [nearest_log2_index(K, 2048.0, 3)];
+  int row = 0;
+  while (row < kSplitRows - 1 && M > kSplitRowM[row]) ++row;
+  int S = kBestSplit[row][nearest_log2_index(N, 768.0, 5)][nearest_log2_index(K, 2048.0, 3)];
   // the largest power of two <= S that K allows (a whole number of 16-byte
   // vectors per slice), preferring slices that are whole line pairs
   while (S > 1 && K % (kVecK * S) != 0) S /= 2;
@@ -189,9 +214,9 @@ KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_
                        bool push = false) {
   *dyn_lds = 0;
   // line-pair tiles stream whole 64-K line pairs per wavefront; panel tiles
-  // whole 64-K steps of the slice
+  // whole 64-K steps of the slice (of each half of it with 32-row tiles)
   if (t.stage == kStageLine && nvec % 32 != 0) return nullptr;
-  if (t.stage == kStagePanel && nvec % 8 != 0) return nullptr;
+  if (t.stage == kStagePanel && nvec % (t.rows == 32 ? 16 : 8) != 0) return nullptr;
   if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
     if (KernelFn fn = lookup(f32out, 1, M, t, push)) {
       *dyn_lds = act_lds_bytes(M, nvec);

@@ -1296,18 +1296,23 @@ __global__ __launch_bounds__(kThreads) void lowm_line_kernel(Args a0, Batch bt) 
 // reduction, and with split_k > 1 it publishes, arrives and (as the owner)
 // folds its 16-column strip, with the counter of that strip.
 // ---------------------------------------------------------------------------
-template <int MB, int R>
+template <int MB, int R, int KW>
 struct PanelShape {
-  static constexpr int BN = 16 * kWaves;               // 64 weight rows, 16 per wavefront
+  static constexpr int WN = kWaves / KW;               // wavefronts along N (16 columns each)
+  static constexpr int BN = 16 * WN;                    // weight rows per workgroup tile
   static constexpr int kPP = 68;                        // u32x4 per 8-row piece (1088 B)
   static constexpr int w_slot = 2 * kPP;                // one wavefront's weight step
-  static constexpr int a_slot = 2 * MB * kPP;           // the activation panel of a step
+  static constexpr int a_half = 2 * MB * kPP;           // the activation panel of one K part
+  static constexpr int a_slot = KW * a_half;            // ... of a step (all KW parts)
   static constexpr int slot_elems = kWaves * w_slot + a_slot;
-  static constexpr int a_loads = (2 * MB + kWaves - 1) / kWaves;   // panel pieces per wavefront
+  static constexpr int a_pieces = KW * 2 * MB;          // panel pieces per step
+  static constexpr int a_loads = (a_pieces + kWaves - 1) / kWaves;   // ... per wavefront
   static constexpr int step_loads = 2 + a_loads;        // vector-memory ops per step per wavefront
   static constexpr int lds_bytes = R * slot_elems * 16;
-  static constexpr bool valid = MB >= 2 && MB <= 4 && R >= 3 && R <= 8 &&
-                                (R - 1) * step_loads <= 63 && lds_bytes <= 128 * 1024;
+  static constexpr int red_floats = (KW - 1) * WN * MB * 4 * kWave;   // K-part reduction
+  static constexpr bool valid = MB >= 2 && MB <= 4 && R >= 3 && R <= 8 && (KW == 1 || KW == 2) &&
+                                (R - 1) * step_loads <= 63 && lds_bytes <= 128 * 1024 &&
+                                red_floats * 4 <= lds_bytes;
 };
 
 template <int N, typename F, int... I>
@@ -1320,9 +1325,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int MB, int R, typename OutT>
+template <int MB, int R, int KW, typename OutT>
 __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict__ ring) {
-  using SH = PanelShape<MB, R>;
+  using SH = PanelShape<MB, R, KW>;
   constexpr int BN = SH::BN;
   constexpr int kPP = SH::kPP;
   constexpr int kSlot = SH::slot_elems;
@@ -1338,11 +1343,15 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
   if (tile * BN >= a.N) return;        // a whole workgroup past the end (grid padding)
+  // Wavefront (wn, kh): 16 columns wn of the tile, K part kh of the slice
+  // (KW 2: the slice's two halves, added in order after the main loop).
+  const int wn = wave % SH::WN, kh = wave / SH::WN;
   const int n0 = tile * BN;
-  const int nw = n0 + 16 * wave;       // this wavefront's first column
+  const int nw = n0 + 16 * wn;         // this wavefront's first column
   const int nvec = a.nvec;
-  const int P = nvec / 8;              // steps in the slice; the launch requires nvec % 8 == 0
-  const size_t kw = (size_t)rank * nvec * kVecK;
+  const int P = nvec / (8 * KW);       // steps per K part; the launch requires nvec % (8*KW) == 0
+  const size_t kr = (size_t)rank * nvec * kVecK;   // the rank's slice
+  const size_t kpart = (size_t)P * 64;             // elements per K part
 
   // Line loads: lane 8q + j fetches 16-byte piece (j - q/2) mod 8 of row q of
   // an 8-row piece and lands at position j of that row in LDS, so that the
@@ -1355,22 +1364,24 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
   for (int i = 0; i < 2; ++i) {
     int n = nw + 8 * i + qr;
     n = n < a.N ? n : a.N - 1;
-    wsrc[i] = a.W + (size_t)n * a.K + kw + piece * kVecK;
+    wsrc[i] = a.W + (size_t)n * a.K + kr + kh * kpart + piece * kVecK;
   }
   // This wavefront's panel pieces: j = wave + 4t (clamped: with MB 3 the
   // last piece is loaded by more than one wavefront, with identical data,
   // and every copy lands before the barrier that publishes the stage).
-  // Piece j holds activation rows 8j .. 8j+7; rows >= M read row M-1: MFMA
-  // output rows are independent and rows >= M are never stored.
+  // Piece j is K part j / (2*MB), activation rows 8*(j % (2*MB)) .. +7; rows
+  // >= M read row M-1: MFMA output rows are independent and rows >= M are
+  // never stored.
   const uint16_t* asrc[SH::a_loads];
   int apos[SH::a_loads];
 #pragma unroll
   for (int t = 0; t < SH::a_loads; ++t) {
     int j = wave + kWaves * t;
-    j = j < 2 * MB ? j : 2 * MB - 1;
-    int m = 8 * j + qr;
+    j = j < SH::a_pieces ? j : SH::a_pieces - 1;
+    const int jk = j / (2 * MB), jj = j - jk * (2 * MB);
+    int m = 8 * jj + qr;
     m = m < a.M ? m : a.M - 1;
-    asrc[t] = a.A + (size_t)m * a.K + kw + piece * kVecK;
+    asrc[t] = a.A + (size_t)m * a.K + kr + jk * kpart + piece * kVecK;
     apos[t] = kWaves * SH::w_slot + j * kPP;
   }
   // MFMA-layout read offsets within a pair of 8-row pieces: row l16, piece 4c+g.
@@ -1426,7 +1437,8 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int b = 0; b < MB; ++b)
-        v[2 + c * MB + b] = lds_read_opaque(slot + kWaves * SH::w_slot + 2 * b * kPP + rpos[c]);
+        v[2 + c * MB + b] =
+            lds_read_opaque(slot + kWaves * SH::w_slot + kh * SH::a_half + 2 * b * kPP + rpos[c]);
     lds_wait(v);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -1482,6 +1494,29 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
   }
   mfma_settle(acc);
   LOWM_TRACE(kTraceLoopEnd);
+  if constexpr (KW == 2) {
+    // The two K halves of each strip: the second half's sums go through LDS
+    // (the ring, which every wavefront has finished reading once all reach
+    // the barrier) and are added to the first's, in that order; the first
+    // half's wavefront carries on alone.
+    float* red = reinterpret_cast<float*>(ring);
+    auto red_at = [&](int b, int i) -> float& { return red[((wn * MB + b) * 4 + i) * kWave + lane]; };
+    barrier_keep_loads();
+    if (kh == 1) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_at(b, i) = acc[b][i];
+    }
+    wait_lgkmcnt0();
+    barrier_keep_loads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[b][i] = acc[b][i] + red_at(b, i);
+    LOWM_TRACE(kTraceReduced);
+  }
 
   if (nw >= a.N) return;               // this wavefront's columns lie past the end of C
   // This lane's sums: block b, register i is C[16b + 4g + i][nw + l16].
@@ -1571,12 +1606,12 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
   LOWM_TRACE(kTraceEnd);
 }
 
-template <int MB, int R, typename OutT>
+template <int MB, int R, int KW, typename OutT>
 __global__ __launch_bounds__(kThreads) void lowm_panel_kernel(Args a0, Batch bt) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const Args a = gemm_args(a0, bt);
-  __shared__ u32x4 ring[R * PanelShape<MB, R>::slot_elems];
-  panel_tile_body<MB, R, OutT>(a, ring);
+  __shared__ u32x4 ring[R * PanelShape<MB, R, KW>::slot_elems];
+  panel_tile_body<MB, R, KW, OutT>(a, ring);
 #endif
 }
 
@@ -1603,9 +1638,12 @@ KernelFn kernel_for() {
     else
       return nullptr;
   } else if constexpr (v.stage == kStagePanel) {
-    // 64-row tiles (16 rows per wavefront), activation panel in LDS
-    if constexpr (ACT == 0 && RG == 4 && PanelShape<MB, v.stages>::valid)
-      return lowm_panel_kernel<MB, v.stages, OutT>;
+    // 64-row tiles (16 rows per wavefront, each the whole K slice) or 32-row
+    // tiles (16 rows per pair of wavefronts, each half the K slice);
+    // activation panel in LDS
+    constexpr int KW = RG == 4 ? 1 : 2;
+    if constexpr (ACT == 0 && (RG == 4 || RG == 2) && PanelShape<MB, v.stages, KW>::valid)
+      return lowm_panel_kernel<MB, v.stages, KW, OutT>;
     else
       return nullptr;
   } else if constexpr (RG <= 2 && Shape<MB, RG, v.stage, v.unroll, v.stages, ACT>::valid) {

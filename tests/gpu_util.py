@@ -63,8 +63,9 @@ def all_tactics(M: int):
     for rows in (16, 32):
         for stage, unroll, stages in VARIANTS:
             out.append(binding.tactic(stage, rows, unroll, stages))
-    for ring in PANEL_RINGS:
-        out.append(binding.tactic("panel", 64, 2, ring))
+    for rows in (64, 32):
+        for ring in PANEL_RINGS:
+            out.append(binding.tactic("panel", rows, 2, ring))
     return out
 
 

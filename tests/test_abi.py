@@ -107,10 +107,15 @@ def test_pick_prefers_line_pairs_where_measured_faster(lib):
 
 def test_pick_panel_tiles_above_16_rows(lib):
     panel = binding.LOWM_STAGE_PANEL
-    for M, N, K, S in [(17, 6144, 4096, 2), (32, 6144, 4096, 1), (64, 6144, 4096, 2),
-                       (64, 49152, 4096, 8), (48, 100, 512, 1)]:
+    # 64-row tiles where they give at least 192 workgroups, else 32-row
+    # tiles that split the K slice in halves (when it has whole 128-K halves)
+    for M, N, K, S, rows in [(17, 6144, 4096, 2, 64), (32, 6144, 4096, 1, 32),
+                             (64, 6144, 4096, 2, 64), (64, 49152, 4096, 8, 64),
+                             (48, 100, 512, 1, 32), (64, 12288, 4096, 1, 64),
+                             (40, 6144, 4096, 4, 64), (33, 2304, 12288, 4, 32),
+                             (64, 6144, 1088, 1, 64)]:
         t = lib.pick_tactic(M, N, K, S)
-        assert (t.stage, t.rows, t.unroll, t.stages) == (panel, 64, 2, 4), (M, N, K, S, t)
+        assert (t.stage, t.rows, t.unroll, t.stages) == (panel, rows, 2, 4), (M, N, K, S, t)
     # a slice that is not whole 64-K steps: register ring
     t = lib.pick_tactic(64, 6144, 1032, 3)
     assert t.stage == binding.LOWM_STAGE_REG
@@ -227,15 +232,24 @@ def test_line_tactic_needs_whole_line_pairs(lib):
 
 
 def test_pick_split_k(lib):
-    # the measured table at its grid points (MI355X, default tactic per split_k)
+    # the measured table at its grid points (MI355X, default tactic per
+    # split_k; profiles/split_k_sweep.md)
     assert lib.pick_split_k(4, 6144, 4096) == 2
     assert lib.pick_split_k(4, 6144, 8192) == 2
     assert lib.pick_split_k(4, 768, 4096) == 4
+    assert lib.pick_split_k(4, 1536, 2048) == 4
     assert lib.pick_split_k(4, 3072, 16384) == 4
     assert lib.pick_split_k(4, 12288, 4096) == 1
     assert lib.pick_split_k(16, 768, 4096) == 4
     assert lib.pick_split_k(16, 6144, 4096) == 1
     assert lib.pick_split_k(16, 24576, 16384) == 1
+    assert lib.pick_split_k(32, 768, 16384) == 8
+    assert lib.pick_split_k(32, 6144, 4096) == 1
+    assert lib.pick_split_k(64, 6144, 4096) == 1
+    assert lib.pick_split_k(64, 3072, 8192) == 4
+    # rows: M <= 8, <= 16, <= 32, else the M 64 measurements
+    assert lib.pick_split_k(9, 1536, 8192) == 8 and lib.pick_split_k(8, 1536, 8192) == 4
+    assert lib.pick_split_k(17, 768, 8192) == 8 and lib.pick_split_k(33, 1536, 2048) == 1
     # always a split_k the launch accepts
     for M in (1, 4, 9, 16, 33, 64):
         for N in (1, 100, 768, 2304, 6144, 100000):

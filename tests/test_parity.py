@@ -118,13 +118,13 @@ def test_ragged(lib, M, N, K, S):
 def test_every_tactic_random(lib):
     """M 20 (two row blocks) with whole 256-K slices: every tactic family
     applies (5 register/LDS variants at 16 rows, 4 at 32, 3 line-pair rings,
-    3 panel rings)."""
+    3 panel rings at 64 rows and 3 at 32)."""
     wl = workloads.Workload("tactics", 20, 300, 2048, 2, seed_a=77, seed_w=78)
     ran = []
     for t in all_tactics(wl.M):
         if check_random(lib, wl, tactic=t, what=repr(t)) is not None:
             ran.append(t)
-    assert len(ran) == 15, ran
+    assert len(ran) == 18, ran
 
 
 def test_every_tactic_small_m_ragged_k(lib):
@@ -221,15 +221,20 @@ PANEL_CASES = [  # M, N, K, S: ragged N (partial strips, wavefronts past the end
 ]
 
 
-@pytest.mark.parametrize("ring", [3, 4, 6])
+@pytest.mark.parametrize("rows,ring", [(64, 3), (64, 4), (64, 6), (32, 3), (32, 4), (32, 6)])
 @pytest.mark.parametrize("M,N,K,S", PANEL_CASES)
-def test_panel_tiles(lib, M, N, K, S, ring):
+def test_panel_tiles(lib, M, N, K, S, rows, ring):
     """Panel tiles (activation panel shared in LDS, each 16-column strip
-    owned by one wavefront through the exchange) against the oracle."""
+    owned by one wavefront, or with 32-row tiles by two that split the K
+    slice in halves, through the exchange) against the oracle.  With 32-row
+    tiles the ring of 6 does not fit LDS for 49..64 rows."""
     wl = workloads.Workload(f"panel_{M}_{N}_{K}_{S}", M, N, K, S, seed_a=M + ring, seed_w=N + S)
-    t = sbg.tactic("panel", 64, 2, ring)
-    v = check_random(lib, wl, tactic=t, what=f"panel ring {ring} {M}x{N}x{K} s{S}")
-    assert v is not None, f"panel ring {ring} is not built for M {M}"
+    t = sbg.tactic("panel", rows, 2, ring)
+    if rows == 32 and ring == 6 and M > 48:
+        assert lib.check_launch(M, N, K, S, tactic=t) == sbg.binding.LOWM_ERR_UNSUPPORTED
+        return
+    v = check_random(lib, wl, tactic=t, what=f"panel {rows}:{ring} {M}x{N}x{K} s{S}")
+    assert v is not None, f"panel {rows} ring {ring} is not built for M {M}"
 
 
 @pytest.mark.parametrize("wl", [w for w in workloads.sweep() if w.M >= 32], ids=lambda w: w.name)
