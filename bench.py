@@ -517,11 +517,17 @@ def cpu_table():
 
 def config_table(lib, dev, steps, reps):
     """One markdown row per configuration: us/call back-to-back and replayed
-    from a graph, GB/s and % of peak, each W streamed from HBM (rotated pool)."""
+    from a graph, GB/s and % of peak, each W streamed from HBM (rotated pool),
+    and the plain streaming read of the same weights through the same pool
+    (the read kernel of the bandwidth probe: its us per W, and the GEMM's
+    excess over it)."""
     import torch
     import workloads
-    print("| workload | tactic | bytes/call | us/call (plain) | us/call (graph) | GB/s | % of 8 TB/s |")
-    print("|---|---|---|---|---|---|---|")
+    from split_bf16_gemm_amd import BwProbe
+    bw = BwProbe()
+    print("| workload | tactic | bytes/call | us/call (plain) | us/call (graph) | GB/s | "
+          "% of 8 TB/s | plain read of W (us) | GEMM - read (us) |")
+    print("|---|---|---|---|---|---|---|---|---|")
     for wl in workloads.ALL:
         M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
         tac = lib.pick_tactic(M, N, K, S)
@@ -539,11 +545,18 @@ def config_table(lib, dev, steps, reps):
                 for _ in range(reps))
         except Exception:  # graph capture is an extra figure
             ug = float("nan")
+        sink = torch.empty(1024 * 256, dtype=torch.int32, device=dev)
+        # the read of each set's W, rotating like the GEMM
+        reads = [lambda W=st[1]: bw.read(W, sink, 1024) for st in pool.sets]
+        for r in reads:
+            r()
+        torch.cuda.synchronize()
+        ur = statistics.median(time_loop(lambda f: f(), reads, steps) for _ in range(reps))
         nbytes = algorithmic_bytes(M, N, K, S)
         gbps = nbytes / us / 1e3
-        stage = repr(tac).split("(")[1].split(",")[0]
-        print(f"| {wl.name} | {stage}:{tac.rows}:{tac.unroll}:{tac.stages} | {nbytes:,} | "
-              f"{us:.2f} | {ug:.2f} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f} |", flush=True)
+        print(f"| {wl.name} | {tactic_text(tac)} | {nbytes:,} | "
+              f"{us:.2f} | {ug:.2f} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f} | "
+              f"{ur:.2f} | {us - ur:+.2f} |", flush=True)
         del pool
         torch.cuda.empty_cache()
 

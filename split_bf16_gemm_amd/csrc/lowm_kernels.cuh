@@ -293,19 +293,26 @@ __device__ __forceinline__ const uint32_t* peer_slot(const uint32_t* slots, size
   return slots + (size_t)(i < rank ? i : i + 1) * E + e;
 }
 
-template <int NW>
-__device__ __forceinline__ void await_published(uint32_t (&w)[NW], const uint32_t* const (&src)[NW],
-                                             uint32_t* fault) {
+// Re-reads, with s_sleep between rounds and for at most kFoldPollTicks, the
+// words of w still zero; word k came from slot(base, k).  The base pointer
+// passes through an empty asm each round, so the addresses are recomputed
+// on this rare path instead of being kept live in registers for the whole
+// kernel.  A word that stays zero sets the fault word.
+template <int NW, typename Slot>
+__device__ __forceinline__ void await_published(uint32_t (&w)[NW], const uint32_t* base,
+                                                Slot slot, uint32_t* fault) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   bool zero = true;
   while (true) {
     __builtin_amdgcn_s_sleep(4);
+    asm volatile("" : "+v"(base));
 #pragma unroll
-    for (int i = 0; i < NW; ++i)
-      if (w[i] == 0u) w[i] = __hip_atomic_load(src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k = 0; k < NW; ++k)
+      if (w[k] == 0u)
+        w[k] = __hip_atomic_load(slot(base, k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     zero = false;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) zero = zero || w[i] == 0u;
+    for (int k = 0; k < NW; ++k) zero = zero || w[k] == 0u;
     if (!__any(zero)) return;
     if (__builtin_amdgcn_s_memrealtime() - t0 > kFoldPollTicks) break;
   }
@@ -316,19 +323,16 @@ template <int SN, int NE>
 __device__ __forceinline__ void fold_owner_n(const uint32_t* slots, size_t E, const int (&e)[NE],
                                              int rank, float (&v)[NE], uint32_t* fault) {
   constexpr int NW = NE * (SN - 1);
+  auto slot = [&](const uint32_t* base, int k) {
+    return peer_slot(base, E, e[k / (SN - 1)], rank, k % (SN - 1));
+  };
   uint32_t w[NW];
-  const uint32_t* src[NW];
 #pragma unroll
-  for (int j = 0; j < NE; ++j)
-#pragma unroll
-    for (int i = 0; i < SN - 1; ++i) {
-      src[j * (SN - 1) + i] = peer_slot(slots, E, e[j], rank, i);
-      w[j * (SN - 1) + i] = load_slot(src[j * (SN - 1) + i]);
-    }
+  for (int k = 0; k < NW; ++k) w[k] = load_slot(slot(slots, k));
   bool zero = false;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) zero = zero || w[i] == 0u;
-  if (__builtin_expect(__any(zero), 0)) await_published(w, src, fault);
+  for (int k = 0; k < NW; ++k) zero = zero || w[k] == 0u;
+  if (__builtin_expect(__any(zero), 0)) await_published(w, slots, slot, fault);
 #pragma unroll
   for (int j = 0; j < NE; ++j) {
     const uint32_t* wj = w + j * (SN - 1);
@@ -352,9 +356,9 @@ __device__ __forceinline__ void fold_owner_any(const uint32_t* slots, size_t E,
     for (int r = 0; r < S; ++r) {
       float p = v[j];
       if (r != rank) {
-        uint32_t w[1] = {load_slot(slots + (size_t)r * E + e[j])};
-        const uint32_t* src[1] = {slots + (size_t)r * E + e[j]};
-        if (__any(w[0] == 0u)) await_published(w, src, fault);
+        auto slot = [&](const uint32_t* base, int) { return base + (size_t)r * E + e[j]; };
+        uint32_t w[1] = {load_slot(slot(slots, 0))};
+        if (__any(w[0] == 0u)) await_published(w, slots, slot, fault);
         p = dec_partial(w[0]);
       }
       acc = (r == 0) ? p : acc + p;
