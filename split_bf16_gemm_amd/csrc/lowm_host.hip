@@ -160,14 +160,14 @@ constexpr int kSplitRowM[kSplitRows] = {8, 16, 32, 64};   // M 4 measured for M 
 constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
     // M <= 8            K: 2048 4096 8192 16384
     {{4, 4, 4, 8},    // N 768
-     {4, 2, 4, 4},    // N 1536
+     {1, 2, 4, 4},    // N 1536
      {1, 2, 2, 4},    // N 3072
      {1, 2, 2, 8},    // N 6144
      {1, 1, 2, 8},    // N 12288
      {1, 1, 2, 8}},   // N 24576
     // 8 < M <= 16
-    {{1, 4, 4, 4},
-     {1, 4, 8, 8},
+    {{4, 4, 4, 4},
+     {1, 2, 8, 8},
      {1, 1, 4, 4},
      {1, 1, 2, 2},
      {1, 1, 1, 1},
@@ -175,12 +175,12 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
     // 16 < M <= 32
     {{4, 4, 8, 8},
      {4, 4, 4, 4},
-     {2, 2, 2, 4},
+     {1, 2, 2, 4},
      {1, 1, 1, 2},
-     {1, 1, 1, 4},
+     {1, 1, 1, 1},
      {1, 1, 2, 2}},
     // 32 < M <= 64
-    {{4, 4, 8, 8},
+    {{1, 4, 8, 8},
      {1, 4, 4, 4},
      {1, 4, 4, 4},
      {1, 1, 1, 2},

@@ -237,7 +237,7 @@ def test_pick_split_k(lib):
     assert lib.pick_split_k(4, 6144, 4096) == 2
     assert lib.pick_split_k(4, 6144, 8192) == 2
     assert lib.pick_split_k(4, 768, 4096) == 4
-    assert lib.pick_split_k(4, 1536, 2048) == 4
+    assert lib.pick_split_k(4, 1536, 8192) == 4
     assert lib.pick_split_k(4, 3072, 16384) == 4
     assert lib.pick_split_k(4, 12288, 4096) == 1
     assert lib.pick_split_k(16, 768, 4096) == 4
