@@ -561,6 +561,78 @@ def config_table(lib, dev, steps, reps):
         torch.cuda.empty_cache()
 
 
+BATCH_CASES = [  # (label, M, [N...], K, split_k)
+    ("Q/K/V: N 6144 + 1024 + 1024, K 4096, split_k 2", 4, [6144, 1024, 1024], 4096, 2),
+    ("gate/up: 2 x N 6144, K 4096, split_k 2", 4, [6144, 6144], 4096, 2),
+    ("8 x N 512, K 4096, split_k 2", 4, [512] * 8, 4096, 2),
+    ("3 x N 2304, K 12288, split_k 4", 4, [2304] * 3, 12288, 4),
+    ("1 x N 6144, K 4096, split_k 2", 4, [6144], 4096, 2),
+]
+
+
+def batched_table(lib, dev, steps, reps):
+    """One markdown row per batch of GEMMs: us per step for one batched launch
+    and for one launch per GEMM, each back-to-back and as `steps` steps
+    captured in one graph and replayed; W from HBM through a rotated pool."""
+    import torch
+    from split_bf16_gemm_amd import binding
+    print("| batch (M 4) | bytes/step | batched | separate | graph, batched | graph, separate | "
+          "GB/s batched (% of 8 TB/s) |")
+    print("|---|---|---|---|---|---|---|")
+    for label, M, Ns, K, S in BATCH_CASES:
+        per_set = sum(2 * K * N + 2 * M * K + 2 * M * N for N in Ns) + \
+            lib.batched_workspace_bytes(M, Ns, K, S)
+        sets = max(2, math.ceil(2 * MALL_BYTES / per_set) + 1)
+        g = torch.Generator(device=dev)
+        g.manual_seed(9000 + len(Ns))
+        pool = []
+        for _ in range(sets):
+            As = [torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for _ in Ns]
+            Ws = [(torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+                  for N in Ns]
+            Cs = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N in Ns]
+            ws_b = torch.zeros(max(1, lib.batched_workspace_bytes(M, Ns, K, S)), dtype=torch.uint8,
+                               device=dev)
+            ws_s = [lib.make_workspace(M, N, K, S, dev) for N in Ns]
+            pool.append((lib.descs(As, Ws, Cs), ws_b, [(A.data_ptr(), W.data_ptr(), C.data_ptr(),
+                                                        0 if w is None else w.data_ptr(), N)
+                                                       for A, W, C, w, N in zip(As, Ws, Cs, ws_s, Ns)],
+                         (As, Ws, Cs, ws_s)))
+        torch.cuda.synchronize()
+
+        def batched(h):
+            def call(item):
+                rc = lib.lib.lowm_gemm_splitk_batched(item[0], len(Ns), M, K, S,
+                                                      item[1].data_ptr() if S > 1 else None, h)
+                if rc:
+                    lib.check(rc)
+            return call
+
+        def separate(h):
+            def call(item):
+                for a, w, c, ws, N in item[2]:
+                    rc = lib.call_raw(a, w, c, M, N, K, S, ws, h)
+                    if rc:
+                        lib.check(rc)
+            return call
+
+        cur = torch.cuda.current_stream(dev).cuda_stream
+        for f in (batched(cur), separate(cur)):
+            for i in range(sets):
+                f(pool[i])
+        torch.cuda.synchronize()
+        ub = statistics.median(time_loop(batched(cur), pool, steps) for _ in range(reps))
+        us_ = statistics.median(time_loop(separate(cur), pool, steps) for _ in range(reps))
+        gb = statistics.median(time_graph(batched, pool, steps, dev) for _ in range(reps))
+        gs = statistics.median(time_graph(separate, pool, steps, dev) for _ in range(reps))
+        nbytes = sum(algorithmic_bytes(M, N, K, S) for N in Ns)
+        gbps = nbytes / ub / 1e3
+        print(f"| {label} | {nbytes:,} | {ub:.2f} | {us_:.2f} | {gb:.2f} | {gs:.2f} | "
+              f"{gbps:.0f} ({100 * gbps / PEAK_HBM_GBPS:.1f} %) |", flush=True)
+        del pool
+        torch.cuda.empty_cache()
+
+
 def time_shape(lib, dev, M, N, K, S, tactic, steps, reps, seed=0):
     """us/call of back-to-back launches of one shape and tactic (None: the
     default), W streamed from HBM through a rotated pool of synthetic input
@@ -671,6 +743,9 @@ def main():
     ap.add_argument("--trace", action="store_true",
                     help="timeline of --workload (and --tactic) from the stress build's "
                          "per-workgroup timestamps; print a markdown table")
+    ap.add_argument("--batched", action="store_true",
+                    help="time batched launches against one launch per GEMM (plain loop and "
+                         "one captured graph of all steps); print a markdown table")
     ap.add_argument("--cpu-table", action="store_true",
                     help="no GPU: time the fp64 oracle (1 and T threads) on the pages' "
                          "shapes and the M-sweep ends; print a markdown table")
@@ -710,6 +785,9 @@ def main():
     lib = sbg.load()
     if args.table:
         config_table(lib, dev, args.steps, args.reps)
+        return
+    if args.batched:
+        batched_table(lib, dev, args.steps, args.reps)
         return
     if args.trace:
         trace_breakdown(dev, workloads.by_name(args.workload), parse_tactic(args.tactic))
