@@ -67,7 +67,8 @@ extern "C" {
 #define LOWM_ERR_UNSUPPORTED (-2)
 /* split_k > 1 with a NULL workspace. */
 #define LOWM_ERR_WORKSPACE (-3)
-/* The kernel launch itself failed; see lowm_last_hip_error(). */
+/* A HIP call failed: the kernel launch, or the stream synchronisation or
+ * copy of lowm_workspace_status; see lowm_last_hip_error(). */
 #define LOWM_ERR_LAUNCH (-4)
 /* lowm_gemm_splitk_noalloc: the sizes need a workspace larger than
  * LOWM_SCRATCH_BYTES. */
@@ -154,9 +155,35 @@ size_t lowm_gemm_splitk_batched_workspace_bytes(const lowm_gemm_desc* gemms, int
  * loop, which this library checks and reports as LOWM_ERR_UNSUPPORTED.) */
 const char* lowm_strerror(int code);
 
-/* hipError_t of the most recent failed launch on the calling thread (0 if
+/* hipError_t of the most recent failed HIP call on the calling thread (0 if
  * none); the cause behind LOWM_ERR_LAUNCH. */
 int lowm_last_hip_error(void);
+
+/* Status of a split-K workspace (the failure detection of the survey's
+ * auxiliary subsystems; the pages' own defects were lost or stale reads,
+ * PR "Fix two synchronization gaps in the MiniMax M3 low-M split-K GEMM",
+ * Description items 1 and 2).  Each 256-byte counter line of the workspace
+ * holds, in word 0, the tile's arrival count and, in word 1, its fault word.
+ * An owner that still finds a peer's partial slot unpublished 1 ms after
+ * every peer has arrived stops waiting, folds the slot as it reads it and
+ * sets the fault word; the library never clears a fault word.  That
+ * launch's C is invalid for the tile, and the workspace must be zeroed
+ * before its next use (the late partial may still land in it).  A
+ * non-zero arrival count after the stream has drained means a launch that
+ * did not complete.
+ *
+ * Waits for the work queued on `stream` (hipStreamSynchronize), copies the
+ * ceil(N / 16) counter lines of `workspace` (a workspace last used by a
+ * launch with N output columns and split_k > 1) to the host and stores the
+ * number of tiles with a set fault word in *faulted_tiles and the number
+ * with a non-zero arrival count in *open_tiles.  For a batched workspace,
+ * call it on each GEMM's part: GEMM g's begins after the
+ * lowm_gemm_splitk_workspace_bytes of GEMMs 0..g-1.  (The built-in scratch
+ * of lowm_gemm_splitk_noalloc is not reachable from here.)  A NULL pointer
+ * or N <= 0 is LOWM_ERR_INVALID_ARG (no HIP call); a failed synchronisation
+ * or copy is LOWM_ERR_LAUNCH. */
+int lowm_workspace_status(const void* workspace, int N, void* stream, int* faulted_tiles,
+                          int* open_tiles);
 
 /*
  * Tactic: how a launch tiles the problem.  lowm_gemm_splitk picks one from

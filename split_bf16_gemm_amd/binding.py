@@ -34,6 +34,7 @@ SITE_STAGE_READ = 2
 SITE_REDUCE = 4
 SITE_PUBLISH = 8
 SITE_FOLD = 16
+SITE_LATE_PUBLISH = 32   # arrive first, store the partial after the stall
 
 
 class Tactic(ctypes.Structure):
@@ -124,6 +125,9 @@ class Library:
         lib.lowm_gemm_splitk_batched_workspace_bytes.argtypes = [ctypes.POINTER(GemmDesc), _i,
                                                                  _i, _i, _i]
         lib.lowm_gemm_splitk_batched_workspace_bytes.restype = ctypes.c_size_t
+        lib.lowm_workspace_status.argtypes = [_vp, _i, _vp, ctypes.POINTER(_i),
+                                              ctypes.POINTER(_i)]
+        lib.lowm_workspace_status.restype = _i
         self.has_stress = hasattr(lib, "lowm_stress_configure")
         if self.has_stress:
             lib.lowm_stress_configure.argtypes = [ctypes.c_uint, _i, _i, _i, _i, _i, ctypes.c_uint]
@@ -319,6 +323,21 @@ class Library:
         if n == 0:
             return None
         return torch.zeros(n, dtype=torch.uint8, device=device)
+
+    def workspace_status(self, workspace: torch.Tensor, N: int, stream=None) -> tuple:
+        """(faulted tiles, tiles with a non-zero arrival count) of a workspace
+        last used by a launch with N output columns, once ``stream`` (default:
+        the current one) has drained."""
+        if workspace is None or not workspace.is_cuda:
+            raise ValueError("workspace_status needs the device workspace tensor")
+        if workspace.numel() * workspace.element_size() < 256 * ((N + 15) // 16):
+            raise ValueError(f"the workspace is too small for N={N}")
+        s = stream if stream is not None else torch.cuda.current_stream(workspace.device)
+        faulted, open_ = ctypes.c_int(0), ctypes.c_int(0)
+        with torch.cuda.device(workspace.device):
+            self.check(self.lib.lowm_workspace_status(workspace.data_ptr(), N, s.cuda_stream,
+                                                      ctypes.byref(faulted), ctypes.byref(open_)))
+        return faulted.value, open_.value
 
     TRACE_SLOTS = 10    # entry, first stage, loop end, reduced, arrived, end, CU, XCD, tile, rank
 

@@ -11,6 +11,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "lowm_types.h"
 
@@ -590,7 +591,7 @@ const char* lowm_strerror(int code) {
       return "unsupported (M > 64, K not a multiple of 8*split_k, split_k > 256, misaligned "
              "pointer, or tactic not in this build)";
     case LOWM_ERR_WORKSPACE: return "split_k > 1 needs a workspace";
-    case LOWM_ERR_LAUNCH: return "kernel launch failed (see lowm_last_hip_error)";
+    case LOWM_ERR_LAUNCH: return "a HIP call failed (see lowm_last_hip_error)";
     case LOWM_ERR_SCRATCH:
       return "the sizes need more workspace than the built-in scratch of "
              "lowm_gemm_splitk_noalloc (LOWM_SCRATCH_BYTES)";
@@ -600,12 +601,36 @@ const char* lowm_strerror(int code) {
 
 int lowm_last_hip_error(void) { return lowm::g_last_hip_error; }
 
+int lowm_workspace_status(const void* workspace, int N, void* stream, int* faulted_tiles,
+                          int* open_tiles) {
+  if (!workspace || N <= 0 || !faulted_tiles || !open_tiles) return LOWM_ERR_INVALID_ARG;
+  const size_t lines = (size_t)(N + 15) / 16;
+  std::vector<uint32_t> host(lines * lowm::kCtrStride);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipMemcpyAsync(host.data(), workspace, host.size() * sizeof(uint32_t),
+                                  hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess) {
+    lowm::g_last_hip_error = (int)err;
+    return LOWM_ERR_LAUNCH;
+  }
+  int faulted = 0, open = 0;
+  for (size_t t = 0; t < lines; ++t) {
+    const uint32_t* line = host.data() + t * lowm::kCtrStride;
+    faulted += line[lowm::kFaultWord] != 0u;
+    open += line[0] != 0u;
+  }
+  *faulted_tiles = faulted;
+  *open_tiles = open;
+  return LOWM_OK;
+}
+
 #ifdef LOWM_STRESS
 // Stress build only: where, on whom and how long the kernels stall.  Applies
 // to every later launch from any thread; not thread-safe.
 int lowm_stress_configure(unsigned site_mask, int rank, int wave, int tile_mod, int tile_sel,
                           int step, unsigned delay_ns) {
-  if (delay_ns > 1000000u) return LOWM_ERR_INVALID_ARG;  // at most 1 ms per stall
+  if (delay_ns > 5000000u) return LOWM_ERR_INVALID_ARG;  // at most 5 ms per stall
   lowm::g_stress.site_mask = site_mask;
   lowm::g_stress.rank = rank;
   lowm::g_stress.wave = wave;

@@ -103,16 +103,22 @@ __device__ __forceinline__ void stall_ticks(uint32_t ticks) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(16);
 }
+__device__ __forceinline__ bool stress_selected(const StressArgs& st, uint32_t site, int rank,
+                                                int wave, int tile, int step) {
+  if (!(st.site_mask & site)) return false;
+  if (st.rank >= 0 && st.rank != rank) return false;
+  if (st.wave >= 0 && st.wave != wave) return false;
+  if (st.tile_mod > 1 && tile % st.tile_mod != st.tile_sel) return false;
+  if (site == kSiteStageRead && st.step >= 0 && st.step != step) return false;
+  return true;
+}
 __device__ __forceinline__ void maybe_stall(const StressArgs& st, uint32_t site, int rank,
                                             int wave, int tile, int step) {
-  if (!(st.site_mask & site)) return;
-  if (st.rank >= 0 && st.rank != rank) return;
-  if (st.wave >= 0 && st.wave != wave) return;
-  if (st.tile_mod > 1 && tile % st.tile_mod != st.tile_sel) return;
-  if (site == kSiteStageRead && st.step >= 0 && st.step != step) return;
-  stall_ticks(st.ticks);
+  if (stress_selected(st, site, rank, wave, tile, step)) stall_ticks(st.ticks);
 }
 #define LOWM_STALL(site, step) maybe_stall(a.stress, (site), rank, wave, tile, (step))
+#define LOWM_LATE_PUBLISH() stress_selected(a.stress, kSiteLatePublish, rank, wave, tile, 0)
+#define LOWM_LATE_STALL() stall_ticks(a.stress.ticks)
 #define LOWM_TRACE(slot)                                                              \
   do {                                                                                \
     if (a.stress.trace && threadIdx.x == 0)                                           \
@@ -132,6 +138,8 @@ __device__ __forceinline__ void maybe_stall(const StressArgs& st, uint32_t site,
   } while (0)
 #else
 #define LOWM_STALL(site, step) ((void)0)
+#define LOWM_LATE_PUBLISH() false
+#define LOWM_LATE_STALL() ((void)0)
 #define LOWM_TRACE(slot) ((void)0)
 #define LOWM_TRACE_IDS() ((void)0)
 #endif
@@ -650,13 +658,19 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   // rank's store lands), so the publisher pays one round trip, not two
   // (measured 0.1-0.3 us per call on the counter-path shapes, no change
   // elsewhere).
-  for (int e = lane; e < E; e += kWave) store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
+  const bool late = LOWM_LATE_PUBLISH();
+  if (!late)
+    for (int e = lane; e < E; e += kWave) store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
   pin_issue();
   uint32_t before = 0;
   if (lane == 0)
     before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
+  if (late) {   // stress build only: the partial lands after the arrival
+    if (before != (uint32_t)(a.S - 1)) LOWM_LATE_STALL();
+    for (int e = lane; e < E; e += kWave) store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
+  }
   if (before != (uint32_t)(a.S - 1)) {   // not the last rank: done
     LOWM_TRACE(kTraceEnd);
     return;
@@ -1545,19 +1559,27 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
   uint32_t* slots = a.part + (size_t)strip * a.S * E;
   uint32_t* ctr = a.ctr + (size_t)strip * kCtrStride;
   LOWM_STALL(kSitePublish, 0);
+  auto publish = [&] {
 #pragma unroll
-  for (int b = 0; b < MB; ++b)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * b + 4 * g + i;
-      if (m < a.M) store_slot(slots + (size_t)rank * E + 16 * m + l16, enc_partial(acc[b][i]));
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * g + i;
+        if (m < a.M) store_slot(slots + (size_t)rank * E + 16 * m + l16, enc_partial(acc[b][i]));
+      }
+  };
+  const bool late = LOWM_LATE_PUBLISH();
+  if (!late) publish();
   pin_issue();           // arrive at once: the owner re-reads any slot still zero
   uint32_t before = 0;
   if (lane == 0)
     before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
+  if (late) {   // stress build only: the partial lands after the arrival
+    if (before != (uint32_t)(a.S - 1)) LOWM_LATE_STALL();
+    publish();
+  }
   if (before != (uint32_t)(a.S - 1)) {
     LOWM_TRACE(kTraceEnd);
     return;

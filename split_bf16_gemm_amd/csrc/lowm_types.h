@@ -38,6 +38,9 @@ enum StressSite : uint32_t {
   kSiteReduce = 4u,       // before writing its sums for the wavefront reduction
   kSitePublish = 8u,      // before storing the rank partial and arriving
   kSiteFold = 16u,        // owner: after the arrival count, before reading partials
+  // A rank arrives first and stores its partial only after the stall (unless
+  // the arrival made it the owner), as if its stores had landed that late.
+  kSiteLatePublish = 32u,
 };
 
 struct StressArgs {

@@ -57,7 +57,7 @@ def test_stress_build_has_its_hook(lib, stress_lib):
 
 
 def test_strerror_names_every_code(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert lib.strerror(code) and "unknown" not in lib.strerror(code)
     assert "unknown" in lib.strerror(-99)
 
@@ -360,3 +360,16 @@ def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     assert fn(FAKE, FAKE, FAKE, 4, 64, 260, 2, None) == binding.LOWM_ERR_UNSUPPORTED
     # the largest sweep shape fits
     assert lib.workspace_bytes(64, 6144, 4096, 8) <= binding.SCRATCH_BYTES
+
+
+def test_workspace_status_validation(lib):
+    """Before any HIP call: NULL pointers and N <= 0 are invalid arguments."""
+    fn = lib.lib.lowm_workspace_status
+    out = ctypes.c_int(7)
+    E = binding
+    assert fn(None, 64, None, ctypes.byref(out), ctypes.byref(out)) == E.LOWM_ERR_INVALID_ARG
+    assert fn(FAKE, 0, None, ctypes.byref(out), ctypes.byref(out)) == E.LOWM_ERR_INVALID_ARG
+    assert fn(FAKE, 64, None, None, ctypes.byref(out)) == E.LOWM_ERR_INVALID_ARG
+    assert fn(FAKE, 64, None, ctypes.byref(out), None) == E.LOWM_ERR_INVALID_ARG
+    assert out.value == 7
+    assert lib.lib.lowm_last_hip_error() == 0

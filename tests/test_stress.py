@@ -10,7 +10,10 @@ ranks and tiles with a bounded s_sleep loop at five sites:
               that did not wait for every reader would overwrite it),
   reduce      before a wavefront hands its sums to the wavefront reduction,
   publish     before a rank stores its partial and arrives,
-  fold        in the owner, after the acquire, before reading the partials.
+  fold        in the owner, after its arrival, before reading the partials,
+and one reordering site, late publish: the rank arrives first and stores its
+partial only after the stall, as if its stores had landed that late (a rank
+arrives without waiting for its stores' acknowledgement).
 Every stalled launch must equal the unstalled launch of the default build
 with the same tactic bit for bit (same kernels, same summation order), and so
 stay within the oracle's bounds.
@@ -190,3 +193,69 @@ def test_split_k4_poll_gives_up_on_a_stalled_middle_rank(libs, rank):
         stress.configure_stress(0)
     assert np.array_equal(got, ref), f"stalled rank {rank}: output differs"
     assert not ws.cpu().numpy().any(), "the workspace was left non-zero"
+
+
+# (workload, tactic, late rank): every epilogue family (line-pair tiles with
+# the early owner, the register ring's counter path, split_k 4, panel strips)
+LATE_CASES = [(workloads.HEADLINE, None, 0), (workloads.HEADLINE, binding.tactic("reg", 16, 8, 2), 0),
+              (workloads.SPLITK4, None, 1), (workloads.by_name("sweep_m64_n6144_k4096_s2"), None, 0)]
+
+
+@pytest.mark.parametrize("case", LATE_CASES, ids=["line_default", "reg_u8_ns2", "line_s4_rank1",
+                                                  "panel_m64"])
+def test_owner_rereads_a_partial_that_lands_after_the_arrival(libs, case):
+    """One rank, on every other tile, arrives and stores its partial 200 us
+    later.  The owner finds that slot still zero, re-reads it until the
+    partial lands and folds it: the output equals the unstalled launch bit for
+    bit, no tile is flagged, no counter is left open and the workspace is
+    zero again."""
+    base, stress = libs
+    wl, tactic, rank = case
+    dev = device()
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    ops = (A, W, ws)
+    say("late publish reference", wl.name, tactic)
+    ref = launch(base, ops, wl, tactic)
+    stress.configure_stress(binding.SITE_LATE_PUBLISH, rank, -1, 2, 1, -1, 200_000)
+    try:
+        say("late publish 200 us, rank", rank, wl.name, tactic)
+        got = launch(stress, ops, wl, tactic)
+    finally:
+        stress.configure_stress(0)
+    assert np.array_equal(got, ref), "a partial that landed late changed the output"
+    assert base.workspace_status(ws, wl.N) == (0, 0), "a tile was flagged or left open"
+    assert not ws.cpu().numpy().any(), "the workspace was left non-zero"
+
+
+def test_owner_gives_up_past_its_bound_and_flags_the_tile(libs):
+    """Rank 0 of every 4th tile at the headline shape arrives and stores its
+    partial 3 ms later, past the owner's 1 ms bound.  Every owner that gives
+    up sets its tile's fault word, which lowm_workspace_status reports; no
+    counter is left open and the other tiles' outputs are unchanged.  Zeroing
+    the workspace clears the flags and the next launch is exact again."""
+    base, stress = libs
+    wl = workloads.HEADLINE
+    dev = device()
+    A, W = (t.to(dev) for t in inputs(wl))
+    ws = base.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    ops = (A, W, ws)
+    say("give-up reference")
+    ref = launch(base, ops, wl, None)
+    tiles = (wl.N + 15) // 16
+    selected = np.arange(tiles) % 4 == 1
+    stress.configure_stress(binding.SITE_LATE_PUBLISH, 0, -1, 4, 1, -1, 3_000_000)
+    try:
+        say("late publish 3 ms, rank 0, every 4th tile")
+        got = launch(stress, ops, wl, None)
+    finally:
+        stress.configure_stress(0)
+    faulted, open_ = base.workspace_status(ws, wl.N)
+    assert open_ == 0, "a counter was left open"
+    assert 1 <= faulted <= int(selected.sum()), f"{faulted} tiles flagged"
+    keep = np.repeat(~selected, 16)[:wl.N]
+    assert np.array_equal(got[:, keep], ref[:, keep]), "an unstalled tile's output changed"
+    ws.zero_()
+    assert base.workspace_status(ws, wl.N) == (0, 0)
+    say("after zeroing the workspace")
+    assert np.array_equal(launch(base, ops, wl, None), ref), "the launch after recovery differs"
