@@ -202,12 +202,23 @@ int lowm_workspace_status(const void* workspace, int N, void* stream, int* fault
  *              be a multiple of 256 (K / split_k % 256 == 0).  rows 16, or
  *              32 with 2 stages; M <= 32.
  *              LOWM_STAGE_PANEL: tiles of 64 rows, 16 per wavefront, each
- *              wavefront walking the whole K slice; W as in LINE (a ring slot
+ *              wavefront walking the whole K slice (or of 32 rows, 16 per
+ *              pair of wavefronts, each of the pair walking one half of the
+ *              slice, the halves added in order); W as in LINE (a ring slot
  *              per wavefront), the activation operand of each 64-K step
  *              ("panel") loaded once per workgroup into an LDS ring of
  *              `stages` steps that all wavefronts read, refilled only after a
- *              workgroup barrier.  rows 64, unroll 2, stages 3, 4 or 6;
- *              17 <= M <= 64; the K slice a multiple of 64.
+ *              workgroup barrier.  rows 64 or 32, unroll 2, stages 3, 4 or 6;
+ *              17 <= M <= 64; the K slice a multiple of 64 (rows 64) or 128
+ *              (rows 32).
+ *              LOWM_STAGE_QUARTER: each wavefront streams one quarter of
+ *              the K slice for the whole tile, both operands (W rows and
+ *              activation rows) through a ring of `stages` 64-K slots of its
+ *              own in LDS, with whole-line direct-to-LDS loads; no barrier in
+ *              the main loop; the four quarter sums are added in order
+ *              through LDS at the end.  rows 16, 32 or 64, unroll 2, stages
+ *              2, 3 or 4 (where LDS and the wait counter allow); the K slice
+ *              a multiple of 256.
  *              LOWM_STAGE_LDS: W goes global -> an LDS ring of `stages`
  *              stages shared by the workgroup; a stage holds 512 K of each of
  *              the tile's rows, each direct-to-LDS load moving 1 KB of one
@@ -219,7 +230,7 @@ int lowm_workspace_status(const void* workspace, int N, void* stream, int* fault
  *              chunks (4, 8 or 16) per wavefront per stage; each wavefront
  *              streams its own contiguous quarter of the K slice.  stages 2.
  *   rows       W rows (output columns) per workgroup tile: 16 or 32 (LINE,
- *              LDS, REG), 64 (PANEL).
+ *              LDS, REG), 64 or 32 (PANEL), 16, 32 or 64 (QUARTER).
  *   waves      wavefronts per workgroup: always 4.
  *   unroll     see stage.
  *   stages     ring depth, see stage.
@@ -230,6 +241,7 @@ int lowm_workspace_status(const void* workspace, int N, void* stream, int* fault
 #define LOWM_STAGE_REG 1
 #define LOWM_STAGE_LINE 3
 #define LOWM_STAGE_PANEL 4
+#define LOWM_STAGE_QUARTER 5
 typedef struct lowm_tactic {
     int stage;
     int rows;

@@ -25,6 +25,7 @@ LOWM_STAGE_LDS = 0
 LOWM_STAGE_REG = 1
 LOWM_STAGE_LINE = 3
 LOWM_STAGE_PANEL = 4
+LOWM_STAGE_QUARTER = 5
 MAX_M = 64
 MAX_SPLIT_K = 256
 
@@ -46,14 +47,15 @@ class Tactic(ctypes.Structure):
 
     def __repr__(self) -> str:
         st = {LOWM_STAGE_LDS: "lds", LOWM_STAGE_REG: "reg", LOWM_STAGE_LINE: "line",
-              LOWM_STAGE_PANEL: "panel"}.get(self.stage, str(self.stage))
+              LOWM_STAGE_PANEL: "panel", LOWM_STAGE_QUARTER: "quarter"}.get(self.stage,
+                                                                          str(self.stage))
         return (f"Tactic({st}, rows={self.rows}, waves={self.waves}, "
                 f"unroll={self.unroll}, stages={self.stages})")
 
 
 def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 4) -> Tactic:
     code = {"lds": LOWM_STAGE_LDS, "reg": LOWM_STAGE_REG, "line": LOWM_STAGE_LINE,
-            "panel": LOWM_STAGE_PANEL}[stage]
+            "panel": LOWM_STAGE_PANEL, "quarter": LOWM_STAGE_QUARTER}[stage]
     return Tactic(code, rows, waves, unroll, stages)
 
 

@@ -108,18 +108,58 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
     }
     return true;
   };
+  // Quarter tiles (each wavefront one quarter of the K slice for the whole
+  // tile, both operands through its own LDS ring).  Measured on MI355X
+  // (bench.py --tactic-matrix) at M 1..64, N 1536..24576, K 4096..16384,
+  // split_k 1..8 against the line-pair and panel tiles:
+  //   - split_k 1, M <= 32: 32-row tiles, ring 3 (16-row tiles where that
+  //     still gives no more than 192 workgroups): M 16, N 6144, K 4096
+  //     10.9 us against 12.3 (line pairs), M 32 12.9 against 13.8 (panel),
+  //     M 4 10.1 against 10.5, M 16 N 24576 32.0 against 33.4;
+  //   - split_k >= 2, 4 < M <= 16: the tile width and ring by the number of
+  //     32-row workgroups W: <= 96 rows 16 ring 3, <= 192 rows 32 ring 3,
+  //     <= 384 rows 16 ring 2, else rows 32 ring 2 (M 16 N 6144 split_k 2 /
+  //     4 / 8: 12.3 / 12.5 / 15.5 us against 14.4 / 15.1 / 17.2);
+  //   - split_k 2, 16 < M <= 32: rows 16 ring 3 where that gives no more than
+  //     192 workgroups, else rows 64 ring 3 (M 32 N 6144: 14.8 against 15.1;
+  //     N 24576: 47.4 against 45.1, taken so that the summation order does
+  //     not depend on N).
+  // The line-pair tiles stay faster for M <= 4 with split_k >= 2 (their last
+  // rank folds without the exchange's round trips), the panel tiles for
+  // M > 32 and for split_k >= 4 above 16 rows.  Every choice below depends
+  // on N only through the tile width and ring, which do not change the
+  // summation order, so a batched launch (picked for its narrowest GEMM)
+  // gives each GEMM the bits of its single call.
+  if (nvec % 32 == 0) {
+    const long w16 = (long)((N + 15) / 16) * S;
+    const long w32 = (long)((N + 31) / 32) * S;
+    auto quarter = [&](int rows, int ring) {
+      t->rows = rows;
+      return provides({kStageQuarter, 2, ring});
+    };
+    if (M <= 16 && S == 1) {
+      if (quarter(32, 3)) return LOWM_OK;
+    } else if (M > 4 && M <= 16) {
+      if (w32 <= 96 ? quarter(16, 3)
+                    : w32 <= 192 ? quarter(32, 3) : w32 <= 384 ? quarter(16, 2) : quarter(32, 2))
+        return LOWM_OK;
+    } else if (M > 16 && M <= 32 && S <= 2) {
+      if (w16 <= 192 ? quarter(16, 3) : S == 1 ? quarter(32, 3) : quarter(64, 3))
+        return LOWM_OK;
+    }
+  }
   // More than 16 activation rows: panel tiles (the activation operand of a
   // step shared in LDS by the four wavefronts), ring of 4 steps.  Measured on
   // MI355X at M 32 and M 64, N 6144, K 4096, split_k 1..8: 1.3-2.1x faster
   // than the line-pair and register tiles at every point; rings of 3 and 6
-  // are within a few percent, 3 slower at M 64.  Where 64-row tiles would
-  // give fewer than 192 workgroups (CUs left idle), 32-row tiles whose two
-  // wavefront pairs split the K slice in halves: M 32 / M 64 at split_k 1,
-  // N 6144: 13.6 / 17.2 us against 18.9 / 21.9 with 64-row tiles; with 192
-  // or more workgroups they lose (split_k 2: 15.7 / 21.3 against 15.1 / 18.5).
+  // are within a few percent, 3 slower at M 64.  Without split-K, 32-row
+  // tiles whose two wavefront pairs split the K slice in halves (twice the
+  // workgroups; M 32 / M 64 at N 6144: 13.6 / 17.2 us against 18.9 / 21.9
+  // with 64-row tiles); with split-K, 64-row tiles (split_k 2: 15.1 / 18.5
+  // against 15.7 / 21.3).  The choice depends on split_k only, so that the
+  // summation order does not depend on N.
   if (M > 16 && nvec % 8 == 0) {
-    const long tiles64 = (N + 63) / 64;
-    t->rows = (tiles64 * S < 192 && nvec % 16 == 0) ? 32 : 64;
+    t->rows = (S == 1 && nvec % 16 == 0) ? 32 : 64;
     if (provides({kStagePanel, 2, 4})) return LOWM_OK;
     t->rows = 64;
     if (provides({kStagePanel, 2, 4})) return LOWM_OK;
@@ -218,6 +258,7 @@ KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_
   // whole 64-K steps of the slice (of each half of it with 32-row tiles)
   if (t.stage == kStageLine && nvec % 32 != 0) return nullptr;
   if (t.stage == kStagePanel && nvec % (t.rows == 32 ? 16 : 8) != 0) return nullptr;
+  if (t.stage == kStageQuarter && nvec % 32 != 0) return nullptr;
   if (nvec % 64 == 0 && act_lds_bytes(M, nvec) <= kActLdsMax) {
     if (KernelFn fn = lookup(f32out, 1, M, t, push)) {
       *dyn_lds = act_lds_bytes(M, nvec);
@@ -300,7 +341,7 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     t = *tactic;
   } else {
     // One tactic serves every GEMM of the launch: pick it for the narrowest
-    // (the only rule that depends on N asks for enough tiles).
+    // (N only sets the tile width and ring, which keep the summation order).
     int n_min = gemms[0].N;
     for (int g = 1; g < count; ++g) n_min = gemms[g].N < n_min ? gemms[g].N : n_min;
     rc = pick(M, n_min, K, S, &t);

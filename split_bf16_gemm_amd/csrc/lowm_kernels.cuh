@@ -1343,6 +1343,114 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
+// The epilogue of one wavefront that holds the whole K-slice sums of a
+// 16-column strip (columns nw .. nw+15) for every activation row: block b,
+// register i of `acc` is C[16b + 4g + i][nw + l16] at lane (g, l16).
+// split_k 1 stores C; otherwise the strip is published to its slots and
+// folded by the last of its ranks to arrive, through the strip's own counter.
+template <int MB, typename OutT>
+__device__ __forceinline__ void strip_epilogue(const Args& a, f32x4 (&acc)[MB], int nw, int rank,
+                                               int tile, int wave, int lane) {
+  (void)tile;
+  (void)wave;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  if (nw >= a.N) return;               // this wavefront's columns lie past the end of C
+  // This lane's sums: block b, register i is C[16b + 4g + i][nw + l16].
+  const int n = nw + l16;
+  if (a.S == 1) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * g + i;
+        if (m < a.M && n < a.N) store_out<OutT>(a, m, n, acc[b][i]);
+      }
+    publish_flags<1, OutT>(a, nw, lane);
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
+
+  // a4: publish this wavefront's partial strip (element (m, c) at word
+  // 16m + c of the rank's slot), then arrive on the strip's counter.
+  const int strip = nw >> 4;
+  const int E = a.M * 16;
+  uint32_t* slots = a.part + (size_t)strip * a.S * E;
+  uint32_t* ctr = a.ctr + (size_t)strip * kCtrStride;
+  LOWM_STALL(kSitePublish, 0);
+  auto publish = [&] {
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * b + 4 * g + i;
+        if (m < a.M) store_slot(slots + (size_t)rank * E + 16 * m + l16, enc_partial(acc[b][i]));
+      }
+  };
+  const bool late = LOWM_LATE_PUBLISH();
+  if (!late) publish();
+  pin_issue();           // arrive at once: the owner re-reads any slot still zero
+  uint32_t before = 0;
+  if (lane == 0)
+    before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __builtin_amdgcn_readfirstlane(before);
+  LOWM_TRACE(kTraceArrived);
+  if (late) {   // stress build only: the partial lands after the arrival
+    if (before != (uint32_t)(a.S - 1)) LOWM_LATE_STALL();
+    publish();
+  }
+  if (before != (uint32_t)(a.S - 1)) {
+    LOWM_TRACE(kTraceEnd);
+    return;
+  }
+
+  // a5/a6: the owner folds its strip in rank order (its own partial from
+  // registers), one block of 4 rows per lane at a time, stores C and returns
+  // every slot and the counter to zero.  Rows >= M fold row 0 again and keep
+  // nothing.
+  LOWM_STALL(kSiteFold, 0);
+  uint32_t* fault = ctr + kFaultWord;
+  float out[MB][4];
+  auto fold_block = [&](auto sn_c, int b) {
+    constexpr int SN = decltype(sn_c)::value;
+    int e[4];
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * b + 4 * g + i;
+      e[i] = 16 * (m < a.M ? m : 0) + l16;
+      v[i] = acc[b][i];
+    }
+    if constexpr (SN > 0) fold_owner_n<SN>(slots, E, e, rank, v, fault);
+    else fold_owner_any(slots, E, e, a.S, rank, v, fault);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[b][i] = v[i];
+  };
+  auto fold_all = [&](auto sn_c) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) fold_block(sn_c, b);
+  };
+  switch (a.S) {
+    case 2: fold_all(std::integral_constant<int, 2>{}); break;
+    case 3: fold_all(std::integral_constant<int, 3>{}); break;
+    case 4: fold_all(std::integral_constant<int, 4>{}); break;
+    case 8: fold_all(std::integral_constant<int, 8>{}); break;
+    default: fold_all(std::integral_constant<int, 0>{}); break;
+  }
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * b + 4 * g + i;
+      if (m >= a.M) continue;
+      if (n < a.N) store_out<OutT>(a, m, n, out[b][i]);
+      clear_slots(slots, E, 16 * m + l16, a.S);
+    }
+  publish_flags<1, OutT>(a, nw, lane);
+  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  LOWM_TRACE(kTraceEnd);
+}
+
 template <int MB, int R, int KW, typename OutT>
 __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict__ ring) {
   using SH = PanelShape<MB, R, KW>;
@@ -1536,100 +1644,7 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
     LOWM_TRACE(kTraceReduced);
   }
 
-  if (nw >= a.N) return;               // this wavefront's columns lie past the end of C
-  // This lane's sums: block b, register i is C[16b + 4g + i][nw + l16].
-  const int n = nw + l16;
-  if (a.S == 1) {
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * b + 4 * g + i;
-        if (m < a.M && n < a.N) store_out<OutT>(a, m, n, acc[b][i]);
-      }
-    publish_flags<1, OutT>(a, nw, lane);
-    LOWM_TRACE(kTraceEnd);
-    return;
-  }
-
-  // a4: publish this wavefront's partial strip (element (m, c) at word
-  // 16m + c of the rank's slot), then arrive on the strip's counter.
-  const int strip = nw >> 4;
-  const int E = a.M * 16;
-  uint32_t* slots = a.part + (size_t)strip * a.S * E;
-  uint32_t* ctr = a.ctr + (size_t)strip * kCtrStride;
-  LOWM_STALL(kSitePublish, 0);
-  auto publish = [&] {
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * b + 4 * g + i;
-        if (m < a.M) store_slot(slots + (size_t)rank * E + 16 * m + l16, enc_partial(acc[b][i]));
-      }
-  };
-  const bool late = LOWM_LATE_PUBLISH();
-  if (!late) publish();
-  pin_issue();           // arrive at once: the owner re-reads any slot still zero
-  uint32_t before = 0;
-  if (lane == 0)
-    before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  before = __builtin_amdgcn_readfirstlane(before);
-  LOWM_TRACE(kTraceArrived);
-  if (late) {   // stress build only: the partial lands after the arrival
-    if (before != (uint32_t)(a.S - 1)) LOWM_LATE_STALL();
-    publish();
-  }
-  if (before != (uint32_t)(a.S - 1)) {
-    LOWM_TRACE(kTraceEnd);
-    return;
-  }
-
-  // a5/a6: the owner folds its strip in rank order (its own partial from
-  // registers), one block of 4 rows per lane at a time, stores C and returns
-  // every slot and the counter to zero.  Rows >= M fold row 0 again and keep
-  // nothing.
-  LOWM_STALL(kSiteFold, 0);
-  uint32_t* fault = ctr + kFaultWord;
-  float out[MB][4];
-  auto fold_block = [&](auto sn_c, int b) {
-    constexpr int SN = decltype(sn_c)::value;
-    int e[4];
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * b + 4 * g + i;
-      e[i] = 16 * (m < a.M ? m : 0) + l16;
-      v[i] = acc[b][i];
-    }
-    if constexpr (SN > 0) fold_owner_n<SN>(slots, E, e, rank, v, fault);
-    else fold_owner_any(slots, E, e, a.S, rank, v, fault);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[b][i] = v[i];
-  };
-  auto fold_all = [&](auto sn_c) {
-#pragma unroll
-    for (int b = 0; b < MB; ++b) fold_block(sn_c, b);
-  };
-  switch (a.S) {
-    case 2: fold_all(std::integral_constant<int, 2>{}); break;
-    case 3: fold_all(std::integral_constant<int, 3>{}); break;
-    case 4: fold_all(std::integral_constant<int, 4>{}); break;
-    case 8: fold_all(std::integral_constant<int, 8>{}); break;
-    default: fold_all(std::integral_constant<int, 0>{}); break;
-  }
-#pragma unroll
-  for (int b = 0; b < MB; ++b)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * b + 4 * g + i;
-      if (m >= a.M) continue;
-      if (n < a.N) store_out<OutT>(a, m, n, out[b][i]);
-      clear_slots(slots, E, 16 * m + l16, a.S);
-    }
-  publish_flags<1, OutT>(a, nw, lane);
-  if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  LOWM_TRACE(kTraceEnd);
+  strip_epilogue<MB, OutT>(a, acc, nw, rank, tile, wave, lane);
 }
 
 template <int MB, int R, int KW, typename OutT>
@@ -1638,6 +1653,206 @@ __global__ __launch_bounds__(kThreads) void lowm_panel_kernel(Args a0, Batch bt)
   const Args a = gemm_args(a0, bt);
   __shared__ u32x4 ring[R * PanelShape<MB, R, KW>::slot_elems];
   panel_tile_body<MB, R, KW, OutT>(a, ring);
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Quarter tiles: the four wavefronts split the rank's K slice into four
+// contiguous quarters, and each streams, for its quarter, both operands of
+// the whole tile (16*NB weight rows and the M activation rows) through a
+// ring of R slots of its own, one 64-K step per slot, with whole-line
+// direct-to-LDS loads (8 rows x 128 B each, rotated as in the line-pair
+// tiles so that the MFMA-layout reads of 16 rows fall in distinct banks).
+// No workgroup barrier in the main loop; every operand byte is written to
+// and read from LDS once (the panel tiles read each activation byte once per
+// wavefront).  After the loop the four quarter sums of each 16-column strip
+// are added in wavefront (K) order through LDS by the strip's wavefront,
+// whose strip epilogue stores or exchanges it.
+// ---------------------------------------------------------------------------
+template <int MB, int NB, int R>
+struct QuarterShape {
+  static constexpr int BN = 16 * NB;             // weight rows per workgroup tile
+  static constexpr int kPP = 68;                 // u32x4 per 8-row piece (1088 B)
+  static constexpr int G = 2 * (NB + MB);        // 8-row pieces (loads) per step
+  static constexpr int slot_elems = G * kPP;     // one wavefront's step
+  static constexpr int lds_bytes = kWaves * R * slot_elems * 16;
+  static constexpr int red_floats = kWaves * NB * MB * 4 * kWave;
+  static constexpr bool valid = MB >= 1 && MB <= 4 && (NB == 1 || NB == 2 || NB == 4) &&
+                                R >= 2 && R <= 8 && (R - 1) * G <= 63 &&
+                                lds_bytes <= 160 * 1024 && red_floats * 4 <= lds_bytes;
+};
+
+template <int MB, int NB, int R, typename OutT>
+__device__ __forceinline__ void quarter_tile_body(const Args& a, u32x4* __restrict__ lds) {
+  using SH = QuarterShape<MB, NB, R>;
+  constexpr int BN = SH::BN;
+  constexpr int G = SH::G;
+  constexpr int kPP = SH::kPP;
+  constexpr int kSlot = SH::slot_elems;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+
+  int tile, rank;
+  decode_tile(a, BN, false, tile, rank);
+  LOWM_TRACE(kTraceEntry);
+  LOWM_TRACE_IDS();
+  if (tile * BN >= a.N) return;        // a whole workgroup past the end (grid padding)
+  const int n0 = tile * BN;
+  // Steps per quarter; the launch requires nvec % 32 == 0 (whole steps).
+  const int P = a.nvec / 32;
+  const size_t k0 = (size_t)rank * a.nvec * kVecK + (size_t)wave * P * 64;
+  u32x4* ring = lds + wave * R * kSlot;
+
+  // Piece t of a step: 8 rows x 128 B, weight rows n0 + 8t .. for t < 2*NB,
+  // then activation rows 8(t - 2*NB) ..; lane 8q + j fetches 16-byte piece
+  // (j - q/2) mod 8 of row q, which lands at position j of that row.  Rows
+  // past the end read the last row: MFMA rows and columns are independent,
+  // and results outside C are never stored.
+  const int qr = lane >> 3;
+  const int piece = ((lane & 7) - (qr >> 1)) & 7;
+  const uint16_t* src[G];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    if (t < 2 * NB) {
+      int n = n0 + 8 * t + qr;
+      n = n < a.N ? n : a.N - 1;
+      src[t] = a.W + (size_t)n * a.K + k0 + piece * kVecK;
+    } else {
+      int m = 8 * (t - 2 * NB) + qr;
+      m = m < a.M ? m : a.M - 1;
+      src[t] = a.A + (size_t)m * a.K + k0 + piece * kVecK;
+    }
+  }
+  // MFMA-layout read offsets within a 16-row block: row l16, piece 4c+g.
+  int rpos[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    rpos[c] = (l16 >> 3) * kPP + (l16 & 7) * 8 + ((4 * c + g + ((l16 & 7) >> 1)) & 7);
+
+  f32x4 acc[NB * MB];                  // [j][b]: column block j, row block b
+#pragma unroll
+  for (int i = 0; i < NB * MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](auto slot_c, int p) {
+    constexpr int SL = decltype(slot_c)::value;
+    u32x4* slot = ring + SL * kSlot;
+    const size_t off = (size_t)p * 64;
+    static_for<G>([&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      __builtin_amdgcn_global_load_lds(src[t] + off,
+                                       (__attribute__((address_space(3))) void*)(slot + t * kPP),
+                                       16, 0, t < 2 * NB ? kStreamAux : 0);
+    });
+    pin_issue();
+  };
+  // Step p out of slot SL (= p mod R).  YOUNGER: how many later steps' loads
+  // may still be in flight once step p's have landed; REFILL: whether step
+  // p+R-1 exists; it goes into the slot step p-1 read, whose reads completed
+  // before its MFMAs (both compile-time, so every wait count is a constant).
+  auto step = [&](auto slot_c, auto younger_c, auto refill_c, int p) {
+    constexpr int SL = decltype(slot_c)::value;
+    wait_vmcnt<decltype(younger_c)::value * G>();
+    LOWM_STALL(kSiteStageRead, p);
+    if (p == 0) LOWM_TRACE(kTraceFirstStage);
+    if constexpr (decltype(refill_c)::value)
+      issue(std::integral_constant<int, (SL + R - 1) % R>{}, p + R - 1);
+    const u32x4* slot = ring + SL * kSlot;
+    u32x4 v[2 * (NB + MB)];            // chunk c: weight blocks, then activation blocks
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t = 0; t < NB + MB; ++t)
+        v[c * (NB + MB) + t] = lds_read_opaque(slot + 2 * t * kPP + rpos[c]);
+    lds_wait(v);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+          acc[j * MB + b] =
+              mfma(v[c * (NB + MB) + NB + b], v[c * (NB + MB) + j], acc[j * MB + b]);
+  };
+
+  LOWM_STALL(kSiteEntry, 0);
+  using T = std::true_type;
+  auto cycle = [&](int p0) {
+    static_for<R>([&](auto s_c) {
+      step(s_c, std::integral_constant<int, R - 2>{}, T{}, p0 + decltype(s_c)::value);
+    });
+  };
+  auto tail = [&](auto rem_c, int p0) {
+    constexpr int REM = decltype(rem_c)::value;
+    static_for<REM>([&](auto i_c) {
+      constexpr int I = decltype(i_c)::value;
+      constexpr int YOUNGER = (REM - 1 - I) < (R - 2) ? (REM - 1 - I) : (R - 2);
+      step(std::integral_constant<int, I % R>{}, std::integral_constant<int, YOUNGER>{},
+           std::integral_constant<bool, (I + R - 1 < REM)>{}, p0 + I);
+    });
+  };
+  int p0 = 0;
+  if (P >= 2 * R - 1) {
+    static_for<R - 1>([&](auto s_c) { issue(s_c, decltype(s_c)::value); });
+    cycle(0);
+    for (p0 = R; p0 + 2 * R - 1 <= P; p0 += R) cycle(p0);
+  } else {
+    static_for<R - 1>([&](auto s_c) {
+      if (decltype(s_c)::value < P) issue(s_c, decltype(s_c)::value);
+    });
+  }
+  static_assert(2 * R - 2 <= 14, "the tail covers at most 14 steps");
+  switch (P - p0) {
+#define LOWM_QUARTER_TAIL(n) \
+    case n: if constexpr (n <= 2 * R - 2) tail(std::integral_constant<int, n>{}, p0); break;
+    LOWM_QUARTER_TAIL(1) LOWM_QUARTER_TAIL(2) LOWM_QUARTER_TAIL(3) LOWM_QUARTER_TAIL(4)
+    LOWM_QUARTER_TAIL(5) LOWM_QUARTER_TAIL(6) LOWM_QUARTER_TAIL(7) LOWM_QUARTER_TAIL(8)
+    LOWM_QUARTER_TAIL(9) LOWM_QUARTER_TAIL(10) LOWM_QUARTER_TAIL(11) LOWM_QUARTER_TAIL(12)
+    LOWM_QUARTER_TAIL(13) LOWM_QUARTER_TAIL(14)
+#undef LOWM_QUARTER_TAIL
+    default: break;
+  }
+  mfma_settle(acc);
+  LOWM_TRACE(kTraceLoopEnd);
+
+  // The quarter sums through LDS (the rings, once every wavefront is done
+  // with its own): wavefront w's block (j, b), register i at
+  // red[(((w * NB + j) * MB + b) * 4 + i) * 64 + lane]; strip j's wavefront
+  // adds the four quarters in order 0..3.
+  float* red = reinterpret_cast<float*>(lds);
+  __syncthreads();
+  LOWM_STALL(kSiteReduce, 0);
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(((wave * NB + j) * MB + b) * 4 + i) * kWave + lane] = acc[j * MB + b][i];
+  __syncthreads();
+  if (wave >= NB) return;
+  f32x4 sum[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = red[((wave * MB + b) * 4 + i) * kWave + lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += red[(((w * NB + wave) * MB + b) * 4 + i) * kWave + lane];
+      sum[b][i] = v;
+    }
+  LOWM_TRACE(kTraceReduced);
+  strip_epilogue<MB, OutT>(a, sum, n0 + 16 * wave, rank, tile, wave, lane);
+}
+
+template <int MB, int NB, int R, typename OutT>
+__global__ __launch_bounds__(kThreads) void lowm_quarter_kernel(Args a0, Batch bt) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const Args a = gemm_args(a0, bt);
+  __shared__ u32x4 lds[kWaves * R * QuarterShape<MB, NB, R>::slot_elems];
+  quarter_tile_body<MB, NB, R, OutT>(a, lds);
 #endif
 }
 
@@ -1670,6 +1885,13 @@ KernelFn kernel_for() {
     constexpr int KW = RG == 4 ? 1 : 2;
     if constexpr (ACT == 0 && (RG == 4 || RG == 2) && PanelShape<MB, v.stages, KW>::valid)
       return lowm_panel_kernel<MB, v.stages, KW, OutT>;
+    else
+      return nullptr;
+  } else if constexpr (v.stage == kStageQuarter) {
+    // 16 * RG weight rows per tile, the K slice in quarters per wavefront;
+    // no staged activation slice
+    if constexpr (ACT == 0 && QuarterShape<MB, RG, v.stages>::valid)
+      return lowm_quarter_kernel<MB, RG, v.stages, OutT>;
     else
       return nullptr;
   } else if constexpr (RG <= 2 && Shape<MB, RG, v.stage, v.unroll, v.stages, ACT>::valid) {

@@ -26,7 +26,8 @@ enum Stage : int {
   kStageLds = LOWM_STAGE_LDS,
   kStageReg = LOWM_STAGE_REG,
   kStageLine = LOWM_STAGE_LINE,
-  kStagePanel = LOWM_STAGE_PANEL
+  kStagePanel = LOWM_STAGE_PANEL,
+  kStageQuarter = LOWM_STAGE_QUARTER
 };
 
 // ---------------------------------------------------------------------------
@@ -116,6 +117,7 @@ constexpr Variant kVariants[] = {
     {kStageLds, 4, 2},   {kStageLds, 4, 3},   {kStageReg, 4, 2},   {kStageReg, 8, 2},
     {kStageReg, 16, 2},  {kStageLine, 2, 2},  {kStageLine, 2, 3},  {kStageLine, 2, 4},
     {kStagePanel, 2, 3}, {kStagePanel, 2, 4}, {kStagePanel, 2, 6},
+    {kStageQuarter, 2, 2}, {kStageQuarter, 2, 3}, {kStageQuarter, 2, 4},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

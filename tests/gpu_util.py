@@ -54,6 +54,7 @@ VARIANTS = [("lds", 4, 2), ("lds", 4, 3),
             ("reg", 4, 2), ("reg", 8, 2), ("reg", 16, 2),
             ("line", 2, 2), ("line", 2, 3), ("line", 2, 4)]
 PANEL_RINGS = (3, 4, 6)
+QUARTER_RINGS = (2, 3, 4)
 
 
 def all_tactics(M: int):
@@ -66,7 +67,19 @@ def all_tactics(M: int):
     for rows in (64, 32):
         for ring in PANEL_RINGS:
             out.append(binding.tactic("panel", rows, 2, ring))
+    for rows in (16, 32, 64):
+        for ring in QUARTER_RINGS:
+            out.append(binding.tactic("quarter", rows, 2, ring))
     return out
+
+
+def quarter_built(M: int, rows: int, ring: int) -> bool:
+    """Whether the build provides quarter tiles of `rows` rows and a ring of
+    `ring` steps for M activation rows: each wavefront's ring slot holds 2
+    pieces of 1088 bytes per 16-row block of either operand; the four rings
+    must fit 160 KB of LDS and their loads the 6-bit wait counter."""
+    loads = 2 * (rows // 16 + (M + 15) // 16)
+    return (ring - 1) * loads <= 63 and 4 * ring * loads * 1088 <= 160 * 1024
 
 
 def run(lib, A_cpu, W_cpu, split_k, f32out=False, tactic=None, workspace=None, dev=None):

@@ -90,30 +90,32 @@ def test_pick_tactic_is_valid_for_every_workload(lib):
     for wl in workloads.ALL:
         t = lib.pick_tactic(wl.M, wl.N, wl.K, wl.split_k)
         assert t.rows in (16, 32, 64) and t.waves == 4
-        if t.stage != binding.LOWM_STAGE_LINE:
+        if t.stage in (binding.LOWM_STAGE_REG, binding.LOWM_STAGE_LDS):
             assert t.rows >= min(32, 16 * ((wl.M + 15) // 16))
         assert lib.check_launch(wl.M, wl.N, wl.K, wl.split_k, tactic=t) == 0
 
 
-def test_pick_prefers_line_pairs_where_measured_faster(lib):
+def test_pick_line_pairs_for_four_rows_or_fewer_with_split(lib):
     line = binding.LOWM_STAGE_LINE
     t = lib.pick_tactic(4, 6144, 4096, 2)        # 8 line pairs per wavefront
     assert (t.stage, t.rows, t.unroll, t.stages) == (line, 16, 2, 4)
-    t = lib.pick_tactic(16, 6144, 4096, 8)       # 2 pairs
-    assert (t.stage, t.stages) == (line, 2)
+    t = lib.pick_tactic(1, 6144, 4096, 8)        # 2 pairs
+    assert (t.stage, t.rows, t.stages) == (line, 16, 2)
+    t = lib.pick_tactic(4, 2304, 12288, 4)       # 12 pairs
+    assert (t.stage, t.rows, t.stages) == (line, 16, 4)
     t = lib.pick_tactic(4, 97, 1032, 3)          # ragged K slice: register ring
     assert t.stage == binding.LOWM_STAGE_REG
 
 
-def test_pick_panel_tiles_above_16_rows(lib):
+def test_pick_panel_tiles_above_32_rows_or_split_k_4(lib):
     panel = binding.LOWM_STAGE_PANEL
-    # 64-row tiles where they give at least 192 workgroups, else 32-row
-    # tiles that split the K slice in halves (when it has whole 128-K halves)
-    for M, N, K, S, rows in [(17, 6144, 4096, 2, 64), (32, 6144, 4096, 1, 32),
-                             (64, 6144, 4096, 2, 64), (64, 49152, 4096, 8, 64),
-                             (48, 100, 512, 1, 32), (64, 12288, 4096, 1, 64),
-                             (40, 6144, 4096, 4, 64), (33, 2304, 12288, 4, 32),
-                             (64, 6144, 1088, 1, 64)]:
+    # 32-row tiles that split the K slice in halves without split-K (when the
+    # slice has whole 128-K halves), 64-row tiles with it
+    for M, N, K, S, rows in [(64, 6144, 4096, 2, 64), (64, 49152, 4096, 8, 64),
+                             (48, 100, 512, 1, 32), (64, 12288, 4096, 1, 32),
+                             (40, 6144, 4096, 4, 64), (33, 2304, 12288, 4, 64),
+                             (64, 6144, 1088, 1, 64), (17, 6144, 4096, 4, 64),
+                             (32, 1536, 8192, 8, 64)]:
         t = lib.pick_tactic(M, N, K, S)
         assert (t.stage, t.rows, t.unroll, t.stages) == (panel, rows, 2, 4), (M, N, K, S, t)
     # a slice that is not whole 64-K steps: register ring
@@ -126,20 +128,30 @@ def test_pick_panel_tiles_above_16_rows(lib):
             binding.LOWM_ERR_UNSUPPORTED
 
 
-def test_pick_32_row_line_tiles_only_where_measured_faster(lib):
-    """32-row line tiles: split_k 1, 5..16 rows, 16 line pairs per wavefront
-    and at least 192 tiles; 16-row tiles otherwise."""
-    line = binding.LOWM_STAGE_LINE
-    for M, N, K, S, rows in [(16, 6144, 4096, 1, 32), (8, 6144, 4096, 1, 32),
-                             (5, 24576, 4096, 1, 32), (12, 6144, 4096, 1, 32),
-                             (16, 6144, 4096, 2, 16),    # split-K
-                             (4, 6144, 4096, 1, 16),     # M <= 4
-                             (16, 768, 4096, 1, 16),     # 24 tiles
-                             (16, 6080, 4096, 1, 16),    # 190 tiles
-                             (16, 6144, 8192, 1, 16),    # 32 pairs
-                             (16, 6144, 2048, 1, 16)]:   # 8 pairs
+def test_pick_quarter_tiles_where_measured_faster(lib):
+    """Quarter tiles: split_k 1 up to 32 rows; 5..16 rows with any split_k;
+    17..32 rows with split_k 2.  The tile width and ring follow the number
+    of workgroups."""
+    quarter = binding.LOWM_STAGE_QUARTER
+    for M, N, K, S, rows, ring in [
+            (16, 6144, 4096, 1, 32, 3), (8, 6144, 4096, 1, 32, 3), (1, 6144, 4096, 1, 32, 3),
+            (4, 24576, 4096, 1, 32, 3),
+            (8, 6144, 4096, 2, 16, 2),       # 384 32-row workgroups
+            (16, 6144, 4096, 4, 32, 2),      # 768
+            (16, 1536, 8192, 2, 16, 3),      # 96
+            (8, 1536, 8192, 4, 32, 3),       # 192
+            (12, 6144, 4096, 8, 32, 2),      # 1536
+            (32, 6144, 4096, 1, 32, 3),      # 384 16-row workgroups
+            (24, 6144, 4096, 2, 64, 3),
+            (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
+            (20, 3072, 4096, 1, 16, 3)]:
         t = lib.pick_tactic(M, N, K, S)
-        assert (t.stage, t.rows) == (line, rows), (M, N, K, S, t)
+        assert (t.stage, t.rows, t.unroll, t.stages) == (quarter, rows, 2, ring), (M, N, K, S, t)
+    # not whole 64-K steps per wavefront, four rows or fewer with split-K,
+    # more than 32 rows, or 17..32 rows with split_k 4: other tiles
+    for M, N, K, S in [(16, 6144, 4160, 1), (4, 6144, 4096, 2), (64, 6144, 4096, 1),
+                       (32, 6144, 4096, 4)]:
+        assert lib.pick_tactic(M, N, K, S).stage != quarter, (M, N, K, S)
 
 
 def call(lib, A=FAKE, W=FAKE, C=FAKE, M=4, N=64, K=256, S=2, ws=FAKE, f32=False, tac=None):
@@ -373,3 +385,21 @@ def test_workspace_status_validation(lib):
     assert fn(FAKE, 64, None, ctypes.byref(out), None) == E.LOWM_ERR_INVALID_ARG
     assert out.value == 7
     assert lib.lib.lowm_last_hip_error() == 0
+
+
+def test_quarter_tiles_built_where_lds_allows(lib):
+    """Quarter tiles exist for every M, rows 16/32/64 and rings 2/3/4 whose
+    four per-wavefront rings fit: 2 pieces of 1088 bytes per 16-row block of
+    either operand per slot, 4 * ring slots within 160 KB of LDS, and
+    (ring - 1) * loads <= 63 outstanding loads; the K slice must be whole
+    64-K steps per wavefront (a multiple of 256)."""
+    for M in (1, 16, 17, 32, 33, 48, 49, 64):
+        for rows in (16, 32, 64):
+            for ring in (2, 3, 4):
+                t = binding.tactic("quarter", rows, 2, ring)
+                loads = 2 * (rows // 16 + (M + 15) // 16)
+                want = (ring - 1) * loads <= 63 and 4 * ring * loads * 1088 <= 160 * 1024
+                rc = lib.check_launch(M, 6144, 4096, 2, tactic=t)
+                assert (rc == binding.LOWM_OK) == want, (M, rows, ring, rc)
+    t = binding.tactic("quarter", 32, 2, 2)
+    assert lib.check_launch(32, 6144, 4096 + 128, 1, tactic=t) == binding.LOWM_ERR_UNSUPPORTED

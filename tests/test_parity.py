@@ -19,7 +19,8 @@ import oracle
 import split_bf16_gemm_amd as sbg
 import workloads
 from checks import assert_bf16, assert_exact_integer, assert_fp32
-from gpu_util import all_tactics, device, inputs, oracle_result, report, run, say, to_bits
+from gpu_util import (all_tactics, device, quarter_built, inputs, oracle_result, report, run,
+                      say, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,21 +119,23 @@ def test_ragged(lib, M, N, K, S):
 def test_every_tactic_random(lib):
     """M 20 (two row blocks) with whole 256-K slices: every tactic family
     applies (5 register/LDS variants at 16 rows, 4 at 32, 3 line-pair rings,
-    3 panel rings at 64 rows and 3 at 32)."""
+    3 panel rings at 64 rows and 3 at 32, 3 quarter rings at 16 and 32 rows
+    and 2 at 64)."""
     wl = workloads.Workload("tactics", 20, 300, 2048, 2, seed_a=77, seed_w=78)
     ran = []
     for t in all_tactics(wl.M):
         if check_random(lib, wl, tactic=t, what=repr(t)) is not None:
             ran.append(t)
-    assert len(ran) == 18, ran
+    assert len(ran) == 26, ran
 
 
 def test_every_tactic_small_m_ragged_k(lib):
     """K / split_k = 344 is neither whole line pairs per wavefront nor whole
     64-K steps, and M 4 is one row block: the register rings of 4 and 8
     chunks and both LDS rings run at 16 and 32 rows (8 tactics); the
-    line-pair and panel tiles, and the 16-chunk register ring (too many
-    registers), return LOWM_ERR_UNSUPPORTED."""
+    line-pair, panel and quarter tiles (whole 64-K steps per wavefront), and
+    the 16-chunk register ring (too many registers), return
+    LOWM_ERR_UNSUPPORTED."""
     wl = workloads.Workload("tactics_k", 4, 97, 1032, 3, seed_a=5, seed_w=6)
     ran = []
     for t in all_tactics(wl.M):
@@ -241,3 +244,30 @@ def test_panel_tiles(lib, M, N, K, S, rows, ring):
 def test_panel_tiles_sweep(lib, wl):
     v = check_random(lib, wl, tactic=sbg.tactic("panel", 64, 2, 4), what=f"panel {wl.name}")
     assert v is not None
+
+
+QUARTER_CASES = [  # M, N, K, S
+    (17, 130, 1280, 5),    # K slice 256: one step per wavefront, generic split_k fold
+    (33, 77, 512, 2),      # ragged N: partial strips, wavefronts past the end
+    (48, 1000, 1536, 3),   # 3 activation blocks, 2 steps per wavefront
+    (64, 64, 4096, 8),     # one tile, split_k 8
+    (64, 6200, 2048, 1),   # no split: direct stores, 8 steps per wavefront
+    (32, 2304, 12288, 4),  # long slices: 12 steps per wavefront
+    (5, 1000, 2048, 2),    # one activation block
+]
+
+
+@pytest.mark.parametrize("rows,ring", [(r, d) for r in (16, 32, 64) for d in (2, 3, 4)])
+@pytest.mark.parametrize("M,N,K,S", QUARTER_CASES)
+def test_quarter_tiles(lib, M, N, K, S, rows, ring):
+    """Quarter tiles (each wavefront one quarter of the K slice for every row
+    of the tile, both operands through its own LDS ring, quarter sums added
+    in order through LDS, then the strip epilogue) against the oracle, where
+    the build provides them; elsewhere the launch is LOWM_ERR_UNSUPPORTED."""
+    wl = workloads.Workload(f"quarter_{M}_{N}_{K}_{S}", M, N, K, S, seed_a=M + ring, seed_w=N + S)
+    t = sbg.tactic("quarter", rows, 2, ring)
+    if not quarter_built(M, rows, ring):
+        assert lib.check_launch(M, N, K, S, tactic=t) == sbg.binding.LOWM_ERR_UNSUPPORTED
+        return
+    v = check_random(lib, wl, tactic=t, what=f"quarter {rows}:{ring} {M}x{N}x{K} s{S}")
+    assert v is not None, f"quarter {rows} ring {ring} is not built for M {M}"

@@ -18,6 +18,8 @@ which are neither needed nor available.
 """
 from __future__ import annotations
 
+import re
+
 from dataclasses import dataclass, field
 
 import torch
@@ -107,7 +109,13 @@ ALL = [INT_EXACT, HEADLINE, SPLITK4, WIDE_N] + sweep()
 
 
 def by_name(name: str) -> Workload:
+    """A named workload, or any shape written mM_nN_kK_sS (seeded from its
+    sizes, the distributions of the random workloads)."""
     for wl in ALL:
         if wl.name == name:
             return wl
+    m = re.fullmatch(r"m(\d+)_n(\d+)_k(\d+)_s(\d+)", name)
+    if m:
+        M, N, K, S = (int(x) for x in m.groups())
+        return Workload(name, M, N, K, S, seed_a=3000 + M, seed_w=4000 + N % 997 + K % 991 + S)
     raise KeyError(name)
