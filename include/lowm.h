@@ -258,10 +258,9 @@ int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out);
 
 /* Host-only: a split_k for these sizes (written to *split_k), chosen from a
  * table of the fastest split_k measured on MI355X (bench.py --split-sweep)
- * over M 4, 16, 32 and 64, N 768 .. 24576, K 2048 .. 16384 (nearest grid
- * point in log2 N and log2 K, the row of the next measured M at or above M;
- * M <= 8 uses the M 4 measurements), reduced to a power of two that K
- * allows.  Any split_k is correct; this one minimises time per call.  (The
+ * over M 4, 8, 16, 32 and 64, N 768 .. 24576, K 2048 .. 16384 (nearest
+ * grid point in log2 N and log2 K, the row of the next measured M at or
+ * above M), reduced to a power of two that K allows.  Any split_k is correct; this one minimises time per call.  (The
  * PR ships split_k 1 and 2, Hardware verification.)  Returns LOWM_OK, or the
  * error code a launch would return for M, N, K. */
 int lowm_pick_split_k(int M, int N, int K, int* split_k);

@@ -190,43 +190,51 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
 
 // split_k for a shape, from a table of the fastest measured on MI355X
 // (bench.py --split-sweep: the default tactic for each split_k, W streamed
-// from HBM through a rotated pool, median of 3 x 40 calls): M 4, 16, 32 and
-// 64, N 768 .. 24576, K 2048 .. 16384, split_k 1, 2, 4, 8.  A shape takes its
-// nearest grid point in log2 N and log2 K and the row of the next measured M
-// at or above its own.  On the grid every entry is the fastest split_k; some
-// neighbours are within a few percent of each other.  split_k pays when the
-// tiles are few and K is long; the larger the partials (M), the less often.
-constexpr int kSplitRows = 4;
-constexpr int kSplitRowM[kSplitRows] = {8, 16, 32, 64};   // M 4 measured for M <= 8
+// from HBM through a rotated pool, median of 3 x 40 calls): M 4, 8, 16, 32
+// and 64, N 768 .. 24576, K 2048 .. 16384, split_k 1, 2, 4, 8.  A shape
+// takes its nearest grid point in log2 N and log2 K and the row of the next
+// measured M at or above its own.  On the grid every entry is the fastest
+// split_k; some neighbours are within a few percent of each other.  split_k
+// pays when the tiles are few and K is long; the larger the partials (M),
+// the less often.
+constexpr int kSplitRows = 5;
+constexpr int kSplitRowM[kSplitRows] = {4, 8, 16, 32, 64};
 constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
-    // M <= 8            K: 2048 4096 8192 16384
+    // M <= 4            K: 2048 4096 8192 16384
     {{4, 4, 4, 8},    // N 768
-     {1, 2, 4, 4},    // N 1536
-     {1, 2, 2, 4},    // N 3072
-     {1, 2, 2, 8},    // N 6144
-     {1, 1, 2, 8},    // N 12288
+     {4, 4, 4, 4},    // N 1536
+     {2, 2, 2, 4},    // N 3072
+     {1, 1, 2, 8},    // N 6144
+     {1, 2, 2, 8},    // N 12288
      {1, 1, 2, 8}},   // N 24576
+    // 4 < M <= 8
+    {{2, 4, 8, 8},
+     {2, 4, 4, 4},
+     {2, 2, 2, 4},
+     {1, 1, 2, 4},
+     {1, 1, 2, 4},
+     {1, 1, 2, 4}},
     // 8 < M <= 16
-    {{4, 4, 4, 4},
-     {1, 2, 8, 8},
-     {1, 1, 4, 4},
-     {1, 1, 2, 2},
-     {1, 1, 1, 1},
-     {1, 1, 1, 1}},
-    // 16 < M <= 32
     {{4, 4, 8, 8},
-     {4, 4, 4, 4},
+     {2, 4, 4, 4},
+     {2, 2, 2, 4},
+     {1, 1, 4, 4},
      {1, 2, 2, 4},
-     {1, 1, 1, 2},
-     {1, 1, 1, 1},
-     {1, 1, 2, 2}},
+     {1, 1, 2, 4}},
+    // 16 < M <= 32
+    {{1, 2, 8, 8},
+     {1, 2, 2, 8},
+     {1, 1, 4, 4},
+     {1, 1, 2, 1},
+     {1, 1, 2, 4},
+     {1, 1, 2, 1}},
     // 32 < M <= 64
     {{1, 4, 8, 8},
-     {1, 4, 4, 4},
+     {1, 4, 8, 8},
      {1, 4, 4, 4},
      {1, 1, 1, 2},
-     {1, 1, 1, 1},
-     {1, 1, 1, 2}}};
+     {1, 2, 2, 2},
+     {1, 1, 2, 2}}};
 
 int nearest_log2_index(double x, double base, int last) {
   const int i = (int)floor(log2(x / base) + 0.5);

@@ -245,22 +245,24 @@ def test_line_tactic_needs_whole_line_pairs(lib):
 
 def test_pick_split_k(lib):
     # the measured table at its grid points (MI355X, default tactic per
-    # split_k; profiles/split_k_sweep.md)
-    assert lib.pick_split_k(4, 6144, 4096) == 2
+    # split_k; bench.py --split-sweep)
+    assert lib.pick_split_k(4, 6144, 4096) == 1
     assert lib.pick_split_k(4, 6144, 8192) == 2
     assert lib.pick_split_k(4, 768, 4096) == 4
     assert lib.pick_split_k(4, 1536, 8192) == 4
     assert lib.pick_split_k(4, 3072, 16384) == 4
-    assert lib.pick_split_k(4, 12288, 4096) == 1
+    assert lib.pick_split_k(4, 12288, 4096) == 2
+    assert lib.pick_split_k(8, 768, 8192) == 8
     assert lib.pick_split_k(16, 768, 4096) == 4
     assert lib.pick_split_k(16, 6144, 4096) == 1
-    assert lib.pick_split_k(16, 24576, 16384) == 1
+    assert lib.pick_split_k(16, 24576, 16384) == 4
     assert lib.pick_split_k(32, 768, 16384) == 8
     assert lib.pick_split_k(32, 6144, 4096) == 1
     assert lib.pick_split_k(64, 6144, 4096) == 1
     assert lib.pick_split_k(64, 3072, 8192) == 4
-    # rows: M <= 8, <= 16, <= 32, else the M 64 measurements
-    assert lib.pick_split_k(9, 1536, 8192) == 8 and lib.pick_split_k(8, 1536, 8192) == 4
+    # rows: M <= 4, <= 8, <= 16, <= 32, else the M 64 measurements
+    assert lib.pick_split_k(4, 768, 2048) == 4 and lib.pick_split_k(5, 768, 2048) == 2
+    assert lib.pick_split_k(9, 1536, 8192) == 4 and lib.pick_split_k(8, 768, 8192) == 8
     assert lib.pick_split_k(17, 768, 8192) == 8 and lib.pick_split_k(33, 1536, 2048) == 1
     # always a split_k the launch accepts
     for M in (1, 4, 9, 16, 33, 64):
