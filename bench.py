@@ -658,6 +658,32 @@ def time_shape(lib, dev, M, N, K, S, tactic, steps, reps, seed=0):
     return us
 
 
+FENCE_WORKLOADS = ["m4_n6144_k4096_s2", "m4_n2304_k12288_s4", "sweep_m1_n6144_k4096_s8",
+                   "sweep_m8_n6144_k4096_s8", "sweep_m16_n6144_k4096_s4",
+                   "sweep_m32_n6144_k4096_s2", "sweep_m64_n6144_k4096_s2"]
+
+
+def fence_ab(dev, steps, reps):
+    """Markdown table: us/call of the default build against the fenced build
+    (release arrival, acquire fence in the owner), default tactic, same
+    pool, alternating the two libraries twice per workload."""
+    import split_bf16_gemm_amd as sbg
+    import workloads
+    libs = {"default": sbg.load(), "fenced": sbg.load("fenced")}
+    print("| workload | tactic | default build (us) | fenced build (us) | fenced / default |")
+    print("|---|---|---|---|---|")
+    for name in FENCE_WORKLOADS:
+        wl = workloads.by_name(name)
+        res = {k: [] for k in libs}
+        for r in range(2):
+            for k, lib in libs.items():
+                res[k].append(time_shape(lib, dev, wl.M, wl.N, wl.K, wl.split_k, None, steps,
+                                         reps, seed=r))
+        d, f = statistics.median(res["default"]), statistics.median(res["fenced"])
+        t = tactic_text(libs["default"].pick_tactic(wl.M, wl.N, wl.K, wl.split_k))
+        print(f"| {name} | {t} | {d:.2f} | {f:.2f} | {f / d:.2f} |", flush=True)
+
+
 def tactic_text(t) -> str:
     stage = repr(t).split("(")[1].split(",")[0]
     return f"{stage}:{t.rows}:{t.unroll}:{t.stages}"
@@ -746,6 +772,10 @@ def main():
     ap.add_argument("--batched", action="store_true",
                     help="time batched launches against one launch per GEMM (plain loop and "
                          "one captured graph of all steps); print a markdown table")
+    ap.add_argument("--fence-ab", action="store_true",
+                    help="time the default build against the fenced comparison build "
+                         "(python -m split_bf16_gemm_amd.build liblowm_fenced.so first); print "
+                         "a markdown table")
     ap.add_argument("--cpu-table", action="store_true",
                     help="no GPU: time the fp64 oracle (1 and T threads) on the pages' "
                          "shapes and the M-sweep ends; print a markdown table")
@@ -795,6 +825,9 @@ def main():
     if args.tactic_matrix:
         names, tacs = (x.split(",") for x in args.tactic_matrix)
         tactic_matrix(lib, dev, names, tacs, args.steps, args.reps)
+        return
+    if args.fence_ab:
+        fence_ab(dev, args.steps, args.reps)
         return
     if args.split_sweep:
         split_sweep(lib, dev, [int(m) for m in args.split_sweep.split(",")], args.steps, args.reps)

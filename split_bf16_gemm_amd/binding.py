@@ -363,9 +363,10 @@ _libs: dict = {}
 
 
 def load(kind: str = "default") -> Library:
-    """The built library: kind 'default' (liblowm.so) or 'stress'."""
+    """The built library: kind 'default' (liblowm.so), 'stress' or 'fenced'."""
     if kind not in _libs:
-        name = {"default": "liblowm.so", "stress": "liblowm_stress.so"}[kind]
+        name = {"default": "liblowm.so", "stress": "liblowm_stress.so",
+                "fenced": "liblowm_fenced.so"}[kind]
         _libs[kind] = Library(LIBDIR / name)
     return _libs[kind]
 

@@ -7,6 +7,10 @@ produces, under split_bf16_gemm_amd/_lib/:
   liblowm_stress.so  the same sources with -DLOWM_STRESS (stall injection)
   libbwprobe.so      streaming read/copy kernels for the HBM ceiling
 
+and, only when named (python -m split_bf16_gemm_amd.build liblowm_fenced.so):
+  liblowm_fenced.so  the same sources with -DLOWM_FENCED (a release arrival
+                     and an acquire fence in the owner; a comparison build)
+
 Each library is linked from objects compiled separately (the kernels of each
 output kind are a translation unit of their own), all in parallel.
 """
@@ -38,6 +42,10 @@ TARGETS = {
     "liblowm.so": (GEMM_SOURCES, []),
     "liblowm_stress.so": (GEMM_SOURCES, ["-DLOWM_STRESS"]),
     "libbwprobe.so": (["bwprobe.hip"], []),
+}
+# built only when named
+OPTIONAL = {
+    "liblowm_fenced.so": (GEMM_SOURCES, ["-DLOWM_FENCED"]),
 }
 
 
@@ -73,7 +81,7 @@ def _compile(lib: str, src: str, extra: list[str], verbose: bool) -> Path:
 
 
 def _link(lib: str, verbose: bool) -> Path:
-    sources, _ = TARGETS[lib]
+    sources, _ = {**TARGETS, **OPTIONAL}[lib]
     out = LIBDIR / lib
     tmp = LIBDIR / f"{lib}.tmp{os.getpid()}"
     _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp),
@@ -86,8 +94,13 @@ def build(verbose: bool = False, only: list[str] | None = None) -> list[Path]:
     """Compile every library (objects in parallel) and return their paths."""
     LIBDIR.mkdir(exist_ok=True)
     OBJDIR.mkdir(exist_ok=True)
-    libs = [l for l in TARGETS if only is None or l in only]
-    jobs = [(lib, src, TARGETS[lib][1]) for lib in libs for src in TARGETS[lib][0]]
+    every = {**TARGETS, **OPTIONAL}
+    unknown = [l for l in (only or []) if l not in every]
+    if unknown:
+        raise ValueError(f"unknown libraries {unknown}; known: {sorted(every)}")
+    libs = [l for l in TARGETS if only is None or l in only] + \
+        [l for l in OPTIONAL if only is not None and l in only]
+    jobs = [(lib, src, every[lib][1]) for lib in libs for src in every[lib][0]]
     workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(lambda j: _compile(*j, verbose), jobs))

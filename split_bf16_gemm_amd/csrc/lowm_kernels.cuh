@@ -144,6 +144,20 @@ __device__ __forceinline__ void maybe_stall(const StressArgs& st, uint32_t site,
 #define LOWM_TRACE_IDS() ((void)0)
 #endif
 
+// The fenced build (-DLOWM_FENCED, a comparison build, never the default):
+// the arrival is a release RMW and the owner issues an acquire fence before
+// it reads its peers' partials, the textbook pairing at agent scope.  The
+// default build needs neither (each slot is written once per launch and
+// read until it is non-zero), and the compiler's agent-scope release and
+// acquire write back and invalidate this XCD's whole L2.
+#ifdef LOWM_FENCED
+#define LOWM_ARRIVE_ORDER __ATOMIC_RELEASE
+#define LOWM_OWNER_FENCE() __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent")
+#else
+#define LOWM_ARRIVE_ORDER __ATOMIC_RELAXED
+#define LOWM_OWNER_FENCE() ((void)0)
+#endif
+
 // ---------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------
@@ -664,7 +678,7 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   pin_issue();
   uint32_t before = 0;
   if (lane == 0)
-    before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __hip_atomic_fetch_add(ctr, 1u, LOWM_ARRIVE_ORDER, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
   if (late) {   // stress build only: the partial lands after the arrival
@@ -681,6 +695,7 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   // with this rank's partial, from LDS, at its own position; every slot read
   // goes back to zero.
   LOWM_STALL(kSiteFold, 0);
+  LOWM_OWNER_FENCE();
   // Two passes: the folds (global loads only, four elements' loads in
   // flight at once; each result replaces the element's wavefront-0 sum in
   // LDS, which nothing else reads), then the stores of C and the clearing
@@ -1392,7 +1407,7 @@ __device__ __forceinline__ void strip_epilogue(const Args& a, f32x4 (&acc)[MB], 
   pin_issue();           // arrive at once: the owner re-reads any slot still zero
   uint32_t before = 0;
   if (lane == 0)
-    before = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __hip_atomic_fetch_add(ctr, 1u, LOWM_ARRIVE_ORDER, __HIP_MEMORY_SCOPE_AGENT);
   before = __builtin_amdgcn_readfirstlane(before);
   LOWM_TRACE(kTraceArrived);
   if (late) {   // stress build only: the partial lands after the arrival
@@ -1409,6 +1424,7 @@ __device__ __forceinline__ void strip_epilogue(const Args& a, f32x4 (&acc)[MB], 
   // every slot and the counter to zero.  Rows >= M fold row 0 again and keep
   // nothing.
   LOWM_STALL(kSiteFold, 0);
+  LOWM_OWNER_FENCE();
   uint32_t* fault = ctr + kFaultWord;
   float out[MB][4];
   auto fold_block = [&](auto sn_c, int b) {

@@ -25,9 +25,11 @@ from gpu_util import device, inputs, say
 pytestmark = pytest.mark.gpu
 
 # (M, N, K, split_k): line-pair tiles with the early owner, panel tiles,
-# the register ring (ragged K slice), line-pair tiles without split-K.
+# the register ring (ragged K slice), quarter tiles of 32 rows without
+# split-K, panel tiles with split_k 4, quarter tiles of 16 and of 64 rows
+# with split_k 2.
 SHAPES = [(4, 1000, 2048, 2), (40, 700, 1536, 3), (9, 333, 1032, 3), (16, 2048, 4096, 1),
-          (64, 512, 4096, 4)]
+          (64, 512, 4096, 4), (12, 1500, 2048, 2), (20, 3000, 2048, 2)]
 
 
 def run32(lib, A, W, S, dev):

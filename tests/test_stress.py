@@ -47,10 +47,12 @@ PLANS = [
 ]
 
 # (workload, tactic): the default tactic at the headline shape is the line-pair
-# tiles; the panel tiles (the default above 16 rows) run at M 64, split_k 2.
+# tiles; the panel tiles run at M 64, split_k 2, the quarter tiles at M 16,
+# split_k 2 (each the default there).
 CASES = [(workloads.HEADLINE, None), (workloads.HEADLINE, binding.tactic("lds", 16, 4, 2)),
          (workloads.HEADLINE, binding.tactic("reg", 16, 8, 2)),
-         (workloads.by_name("sweep_m64_n6144_k4096_s2"), None)]
+         (workloads.by_name("sweep_m64_n6144_k4096_s2"), None),
+         (workloads.by_name("sweep_m16_n6144_k4096_s2"), None)]
 
 
 @pytest.fixture(scope="module")
@@ -68,7 +70,8 @@ def launch(lib, ops, wl, tactic):
     return to_bits(out)
 
 
-@pytest.mark.parametrize("case", CASES, ids=["line_default", "lds_ns2", "reg_u8_ns2", "panel_m64"])
+@pytest.mark.parametrize("case", CASES, ids=["line_default", "lds_ns2", "reg_u8_ns2", "panel_m64",
+                                          "quarter_m16"])
 @pytest.mark.parametrize("plan", PLANS, ids=[p[0] for p in PLANS])
 def test_under_stalls(libs, plan, case):
     base, stress = libs
@@ -196,13 +199,15 @@ def test_split_k4_poll_gives_up_on_a_stalled_middle_rank(libs, rank):
 
 
 # (workload, tactic, late rank): every epilogue family (line-pair tiles with
-# the early owner, the register ring's counter path, split_k 4, panel strips)
+# the early owner, the register ring's counter path, split_k 4, the strips of
+# the panel and of the quarter tiles)
 LATE_CASES = [(workloads.HEADLINE, None, 0), (workloads.HEADLINE, binding.tactic("reg", 16, 8, 2), 0),
-              (workloads.SPLITK4, None, 1), (workloads.by_name("sweep_m64_n6144_k4096_s2"), None, 0)]
+              (workloads.SPLITK4, None, 1), (workloads.by_name("sweep_m64_n6144_k4096_s2"), None, 0),
+              (workloads.by_name("sweep_m16_n6144_k4096_s2"), None, 1)]
 
 
 @pytest.mark.parametrize("case", LATE_CASES, ids=["line_default", "reg_u8_ns2", "line_s4_rank1",
-                                                  "panel_m64"])
+                                                  "panel_m64", "quarter_m16_rank1"])
 def test_owner_rereads_a_partial_that_lands_after_the_arrival(libs, case):
     """One rank, on every other tile, arrives and stores its partial 200 us
     later.  The owner finds that slot still zero, re-reads it until the
