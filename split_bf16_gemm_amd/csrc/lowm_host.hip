@@ -120,16 +120,20 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
   //     32-row workgroups W: <= 96 rows 16 ring 3, <= 192 rows 32 ring 3,
   //     <= 384 rows 16 ring 2, else rows 32 ring 2 (M 16 N 6144 split_k 2 /
   //     4 / 8: 12.3 / 12.5 / 15.5 us against 14.4 / 15.1 / 17.2);
+  //   - split_k 1, M > 32: rows 16 ring 3 where that gives no more than 192
+  //     workgroups, else rows 32 ring 3 up to 384 workgroups, else rows 64
+  //     ring 2 (M 64 N 6144: 17.1 against 17.6 for the panel tiles; N 24576:
+  //     51.7 against 56.6 for 32-row and 48.7 for 64-row panel tiles, taken
+  //     so that the summation order does not depend on N);
   //   - split_k 2, 16 < M <= 32: rows 16 ring 3 where that gives no more than
   //     192 workgroups, else rows 64 ring 3 (M 32 N 6144: 14.8 against 15.1;
-  //     N 24576: 47.4 against 45.1, taken so that the summation order does
-  //     not depend on N).
+  //     N 24576: 47.4 against 45.1, again one order for every N).
   // The line-pair tiles stay faster for M <= 4 with split_k >= 2 (their last
   // rank folds without the exchange's round trips), the panel tiles for
-  // M > 32 and for split_k >= 4 above 16 rows.  Every choice below depends
-  // on N only through the tile width and ring, which do not change the
-  // summation order, so a batched launch (picked for its narrowest GEMM)
-  // gives each GEMM the bits of its single call.
+  // M > 32 with split-K and for split_k >= 4 above 16 rows.  Every choice
+  // below depends on N only through the tile width and ring, which do not
+  // change the summation order, so a batched launch (picked for its
+  // narrowest GEMM) gives each GEMM the bits of its single call.
   if (nvec % 32 == 0) {
     const long w16 = (long)((N + 15) / 16) * S;
     const long w32 = (long)((N + 31) / 32) * S;
@@ -143,24 +147,23 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
       if (w32 <= 96 ? quarter(16, 3)
                     : w32 <= 192 ? quarter(32, 3) : w32 <= 384 ? quarter(16, 2) : quarter(32, 2))
         return LOWM_OK;
-    } else if (M > 16 && M <= 32 && S <= 2) {
-      if (w16 <= 192 ? quarter(16, 3) : S == 1 ? quarter(32, 3) : quarter(64, 3))
+    } else if (M > 16 && S == 1) {
+      if (w16 <= 192 ? quarter(16, 3)
+                     : (M <= 32 || w32 <= 384) ? quarter(32, 3) : quarter(64, 2))
         return LOWM_OK;
+    } else if (M > 16 && M <= 32 && S == 2) {
+      if (w16 <= 192 ? quarter(16, 3) : quarter(64, 3)) return LOWM_OK;
     }
   }
   // More than 16 activation rows: panel tiles (the activation operand of a
   // step shared in LDS by the four wavefronts), ring of 4 steps.  Measured on
   // MI355X at M 32 and M 64, N 6144, K 4096, split_k 1..8: 1.3-2.1x faster
   // than the line-pair and register tiles at every point; rings of 3 and 6
-  // are within a few percent, 3 slower at M 64.  Without split-K, 32-row
-  // tiles whose two wavefront pairs split the K slice in halves (twice the
-  // workgroups; M 32 / M 64 at N 6144: 13.6 / 17.2 us against 18.9 / 21.9
-  // with 64-row tiles); with split-K, 64-row tiles (split_k 2: 15.1 / 18.5
-  // against 15.7 / 21.3).  The choice depends on split_k only, so that the
-  // summation order does not depend on N.
+  // are within a few percent, 3 slower at M 64.  64-row tiles: with split-K
+  // they beat the 32-row tiles whose wavefront pairs split the K slice in
+  // halves (split_k 2, M 32 / M 64: 15.1 / 18.5 us against 15.7 / 21.3),
+  // which win only without split-K, where the quarter tiles win in turn.
   if (M > 16 && nvec % 8 == 0) {
-    t->rows = (S == 1 && nvec % 16 == 0) ? 32 : 64;
-    if (provides({kStagePanel, 2, 4})) return LOWM_OK;
     t->rows = 64;
     if (provides({kStagePanel, 2, 4})) return LOWM_OK;
   }
@@ -222,19 +225,19 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
      {1, 2, 2, 4},
      {1, 1, 2, 4}},
     // 16 < M <= 32
-    {{1, 2, 8, 8},
+    {{1, 2, 2, 8},
      {1, 2, 2, 8},
      {1, 1, 4, 4},
-     {1, 1, 2, 1},
-     {1, 1, 2, 4},
+     {1, 1, 2, 2},
+     {1, 4, 2, 4},
      {1, 1, 2, 1}},
     // 32 < M <= 64
-    {{1, 4, 8, 8},
-     {1, 4, 8, 8},
-     {1, 4, 4, 4},
-     {1, 1, 1, 2},
-     {1, 2, 2, 2},
-     {1, 1, 2, 2}}};
+    {{1, 1, 8, 8},
+     {1, 1, 8, 8},
+     {1, 1, 4, 4},
+     {1, 1, 2, 2},
+     {1, 1, 2, 2},
+     {1, 1, 1, 2}}};
 
 int nearest_log2_index(double x, double base, int last) {
   const int i = (int)floor(log2(x / base) + 0.5);

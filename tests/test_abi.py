@@ -107,15 +107,14 @@ def test_pick_line_pairs_for_four_rows_or_fewer_with_split(lib):
     assert t.stage == binding.LOWM_STAGE_REG
 
 
-def test_pick_panel_tiles_above_32_rows_or_split_k_4(lib):
+def test_pick_panel_tiles_above_32_rows_with_split_or_split_k_4(lib):
     panel = binding.LOWM_STAGE_PANEL
-    # 32-row tiles that split the K slice in halves without split-K (when the
-    # slice has whole 128-K halves), 64-row tiles with it
+    # 64-row tiles; without split-K only where the K slice is not whole 64-K
+    # steps per wavefront (no quarter tiles)
     for M, N, K, S, rows in [(64, 6144, 4096, 2, 64), (64, 49152, 4096, 8, 64),
-                             (48, 100, 512, 1, 32), (64, 12288, 4096, 1, 32),
-                             (40, 6144, 4096, 4, 64), (33, 2304, 12288, 4, 64),
-                             (64, 6144, 1088, 1, 64), (17, 6144, 4096, 4, 64),
-                             (32, 1536, 8192, 8, 64)]:
+                             (40, 6144, 4096, 4, 64),
+                             (33, 2304, 12288, 4, 64), (64, 6144, 1088, 1, 64),
+                             (17, 6144, 4096, 4, 64), (32, 1536, 8192, 8, 64)]:
         t = lib.pick_tactic(M, N, K, S)
         assert (t.stage, t.rows, t.unroll, t.stages) == (panel, rows, 2, 4), (M, N, K, S, t)
     # a slice that is not whole 64-K steps: register ring
@@ -129,7 +128,7 @@ def test_pick_panel_tiles_above_32_rows_or_split_k_4(lib):
 
 
 def test_pick_quarter_tiles_where_measured_faster(lib):
-    """Quarter tiles: split_k 1 up to 32 rows; 5..16 rows with any split_k;
+    """Quarter tiles: split_k 1 for every M; 5..16 rows with any split_k;
     17..32 rows with split_k 2.  The tile width and ring follow the number
     of workgroups."""
     quarter = binding.LOWM_STAGE_QUARTER
@@ -144,12 +143,19 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (32, 6144, 4096, 1, 32, 3),      # 384 16-row workgroups
             (24, 6144, 4096, 2, 64, 3),
             (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
-            (20, 3072, 4096, 1, 16, 3)]:
+            (20, 3072, 4096, 1, 16, 3),
+            (64, 6144, 4096, 1, 32, 3),      # 192 32-row workgroups
+            (64, 12288, 4096, 1, 32, 3),     # 384
+            (48, 24576, 4096, 1, 64, 2),     # 768
+            (64, 2304, 12288, 1, 16, 3),     # 144 16-row workgroups
+            (32, 24576, 4096, 1, 32, 3),     # up to 32 rows: 32-row tiles
+            (48, 100, 512, 1, 16, 3)]:
         t = lib.pick_tactic(M, N, K, S)
         assert (t.stage, t.rows, t.unroll, t.stages) == (quarter, rows, 2, ring), (M, N, K, S, t)
     # not whole 64-K steps per wavefront, four rows or fewer with split-K,
-    # more than 32 rows, or 17..32 rows with split_k 4: other tiles
-    for M, N, K, S in [(16, 6144, 4160, 1), (4, 6144, 4096, 2), (64, 6144, 4096, 1),
+    # more than 32 rows with split-K, or 17..32 rows with split_k 4: other
+    # tiles
+    for M, N, K, S in [(16, 6144, 4160, 1), (4, 6144, 4096, 2), (64, 6144, 4096, 2),
                        (32, 6144, 4096, 4)]:
         assert lib.pick_tactic(M, N, K, S).stage != quarter, (M, N, K, S)
 
@@ -263,7 +269,8 @@ def test_pick_split_k(lib):
     # rows: M <= 4, <= 8, <= 16, <= 32, else the M 64 measurements
     assert lib.pick_split_k(4, 768, 2048) == 4 and lib.pick_split_k(5, 768, 2048) == 2
     assert lib.pick_split_k(9, 1536, 8192) == 4 and lib.pick_split_k(8, 768, 8192) == 8
-    assert lib.pick_split_k(17, 768, 8192) == 8 and lib.pick_split_k(33, 1536, 2048) == 1
+    assert lib.pick_split_k(17, 768, 8192) == 2 and lib.pick_split_k(33, 1536, 2048) == 1
+    assert lib.pick_split_k(64, 768, 8192) == 8 and lib.pick_split_k(64, 768, 4096) == 1
     # always a split_k the launch accepts
     for M in (1, 4, 9, 16, 33, 64):
         for N in (1, 100, 768, 2304, 6144, 100000):
