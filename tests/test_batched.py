@@ -23,7 +23,9 @@ CASES = [
     (1, [6144] * 8, 4096, 8),              # the largest batch
     (4, [768], 4096, 2),                   # a batch of one
     (8, [6144, 6144], 4096, 1),            # 32-row line tiles for every GEMM
-    (8, [6144, 1024], 4096, 1),            # 16-row tiles for the batch, 32-row alone
+    (8, [6144, 1024], 4096, 1),            # quarter tiles, one width for every N
+    (24, [6144, 512], 4096, 2),            # quarter tiles: 16 rows for the batch, 64 alone
+    (64, [6144, 1024], 4096, 1),           # quarter tiles: 16 rows for the batch, 32 alone
 ]
 
 
