@@ -1420,31 +1420,44 @@ __device__ __forceinline__ void strip_epilogue(const Args& a, f32x4 (&acc)[MB], 
   }
 
   // a5/a6: the owner folds its strip in rank order (its own partial from
-  // registers), one block of 4 rows per lane at a time, stores C and returns
-  // every slot and the counter to zero.  Rows >= M fold row 0 again and keep
-  // nothing.
+  // registers), stores C and returns every slot and the counter to zero.
+  // The peers' slots of BPC blocks of 4 rows per lane are loaded at once
+  // (all blocks for split_k 2, two for 3 and 4, one above), so the fold
+  // waits for one round trip per group, not per block.  Rows >= M fold row 0
+  // again and keep nothing.
   LOWM_STALL(kSiteFold, 0);
   LOWM_OWNER_FENCE();
   uint32_t* fault = ctr + kFaultWord;
   float out[MB][4];
-  auto fold_block = [&](auto sn_c, int b) {
+  auto fold_blocks = [&](auto sn_c, auto bpc_c, int b0) {
     constexpr int SN = decltype(sn_c)::value;
-    int e[4];
-    float v[4];
+    constexpr int BPC = decltype(bpc_c)::value;
+    int e[4 * BPC];
+    float v[4 * BPC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * b + 4 * g + i;
-      e[i] = 16 * (m < a.M ? m : 0) + l16;
-      v[i] = acc[b][i];
-    }
+    for (int j = 0; j < BPC; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * (b0 + j) + 4 * g + i;
+        e[4 * j + i] = 16 * (m < a.M ? m : 0) + l16;
+        v[4 * j + i] = acc[b0 + j][i];
+      }
     if constexpr (SN > 0) fold_owner_n<SN>(slots, E, e, rank, v, fault);
     else fold_owner_any(slots, E, e, a.S, rank, v, fault);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[b][i] = v[i];
+    for (int j = 0; j < BPC; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[b0 + j][i] = v[4 * j + i];
   };
   auto fold_all = [&](auto sn_c) {
+    constexpr int SN = decltype(sn_c)::value;
+    constexpr int BPC0 = SN == 2 ? MB : (SN == 3 || SN == 4) ? 2 : 1;
+    constexpr int BPC = BPC0 < MB ? BPC0 : MB;
 #pragma unroll
-    for (int b = 0; b < MB; ++b) fold_block(sn_c, b);
+    for (int b0 = 0; b0 + BPC <= MB; b0 += BPC)
+      fold_blocks(sn_c, std::integral_constant<int, BPC>{}, b0);
+    if constexpr (MB % BPC != 0)
+      fold_blocks(sn_c, std::integral_constant<int, MB % BPC>{}, MB - MB % BPC);
   };
   switch (a.S) {
     case 2: fold_all(std::integral_constant<int, 2>{}); break;
