@@ -684,6 +684,50 @@ def fence_ab(dev, steps, reps):
         print(f"| {name} | {t} | {d:.2f} | {f:.2f} | {f / d:.2f} |", flush=True)
 
 
+PUSH_WORKLOADS = ["m4_n6144_k4096_s2", "m4_n2304_k12288_s4", "sweep_m1_n6144_k4096_s1",
+                  "sweep_m16_n6144_k4096_s2", "sweep_m64_n6144_k4096_s2"]
+
+
+def push_ab(lib, dev, steps, reps):
+    """Markdown table: us/call of lowm_gemm_splitk against lowm_gemm_splitk_push
+    (the owner also writes its tile to an exchange buffer and raises one flag
+    per 16 columns), default tactic, the same rotated pool."""
+    import torch
+    import workloads
+    print("| workload | tactic | plain (us) | push (us) | push - plain (us) |")
+    print("|---|---|---|---|---|")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for name in PUSH_WORKLOADS:
+        wl = workloads.by_name(name)
+        M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
+        per_set = 2 * K * N + 2 * M * K + 4 * M * N + lib.workspace_bytes(M, N, K, S)
+        sets = max(2, math.ceil(2 * MALL_BYTES / per_set) + 1)
+        pool = Pool(lib, wl, sets, dev)
+        bufs = [(torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                 torch.zeros((N + 15) // 16, dtype=torch.int32, device=dev)) for _ in range(sets)]
+        ptrs = [p + (b.data_ptr(), f.data_ptr()) for p, (b, f) in zip(pool.ptrs, bufs)]
+        plain = make_caller(lib, wl, None, stream)
+        fn = lib.lib.lowm_gemm_splitk_push
+
+        def push(p):
+            rc = fn(p[0], p[1], p[2], M, N, K, S, p[3], p[4], N, p[5], 1, stream, None)
+            if rc:
+                lib.check(rc)
+        for i in range(max(10, sets)):
+            plain(ptrs[i % sets])
+            push(ptrs[i % sets])
+        torch.cuda.synchronize()
+        res = {"plain": [], "push": []}
+        for _ in range(reps):
+            res["plain"].append(time_loop(plain, ptrs, steps))
+            res["push"].append(time_loop(push, ptrs, steps))
+        a, b = statistics.median(res["plain"]), statistics.median(res["push"])
+        t = tactic_text(lib.pick_tactic(M, N, K, S))
+        print(f"| {name} | {t} | {a:.2f} | {b:.2f} | {b - a:+.2f} |", flush=True)
+        del pool, bufs
+        torch.cuda.empty_cache()
+
+
 def tactic_text(t) -> str:
     stage = repr(t).split("(")[1].split(",")[0]
     return f"{stage}:{t.rows}:{t.unroll}:{t.stages}"
@@ -776,6 +820,9 @@ def main():
                     help="time the default build against the fenced comparison build "
                          "(python -m split_bf16_gemm_amd.build liblowm_fenced.so first); print "
                          "a markdown table")
+    ap.add_argument("--push-ab", action="store_true",
+                    help="time the push epilogue entry point against the plain one; print a "
+                         "markdown table")
     ap.add_argument("--cpu-table", action="store_true",
                     help="no GPU: time the fp64 oracle (1 and T threads) on the pages' "
                          "shapes and the M-sweep ends; print a markdown table")
@@ -825,6 +872,9 @@ def main():
     if args.tactic_matrix:
         names, tacs = (x.split(",") for x in args.tactic_matrix)
         tactic_matrix(lib, dev, names, tacs, args.steps, args.reps)
+        return
+    if args.push_ab:
+        push_ab(lib, dev, args.steps, args.reps)
         return
     if args.fence_ab:
         fence_ab(dev, args.steps, args.reps)
