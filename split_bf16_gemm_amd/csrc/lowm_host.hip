@@ -66,20 +66,24 @@ KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t, bool push = f
 constexpr size_t kActLdsMax = 48 * 1024;
 size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
 
-// Default tactic.  Where the K slice is whole 64-K line pairs per wavefront
-// (K / split_k % 256 == 0) and M <= 32: line-pair tiles of 16 rows, a ring of
-// 4 slots for M <= 4 with 8..15 pairs per wavefront and of 2 otherwise; not
-// for M > 16 with 16 or more pairs, where the register ring below is faster.
-// Measured on MI355X at N 6144, K 4096, M 1..32, split_k 1..8, and at
-// N 2304 K 12288 split_k 4 and N 49152 K 4096 split_k 2: the line tiles
-// beat the register ring by 3-30 % everywhere else.
-// Otherwise tiles of 16 weight rows for M <= 16 and 32 above (two row
-// groups share each activation load) in a register ring: each of the four
-// wavefronts streams cpw = ceil(chunks / 4) contiguous chunks of its slice.
-// When cpw <= 16 the best ring issues the whole range in its first stage
-// (unroll = the smallest power of two >= cpw, 2 stages); for longer ranges a
-// 4-chunk, 2-stage ring beats deeper ones.  Fall back to other rings, then
-// the LDS variants, when the build has no such instantiation for this M.
+// Default tactic, in order: quarter tiles where the rules below name them,
+// panel tiles above 16 rows, line-pair tiles, the register ring.
+// Line-pair tiles (the default for M <= 4 with split-K, where the K slice is
+// whole 64-K line pairs per wavefront): 16 rows, a ring of 4 slots for
+// M <= 4 with 8..15 pairs per wavefront and of 2 otherwise.  Measured on
+// MI355X at the three shapes of the pages (N 6144 K 4096 split_k 2,
+// N 2304 K 12288 split_k 4, N 49152 K 4096 split_k 2) and M 1 at split_k
+// 2..8: 2-11 % faster than the quarter tiles there (the tile's last rank
+// folds without the exchange's round trips), 19-25 % faster than the
+// register ring.
+// Register ring (slices that are not whole 64-K steps): tiles of 16 weight
+// rows for M <= 16 and 32 above (two row groups share each activation load);
+// each of the four wavefronts streams cpw = ceil(chunks / 4) contiguous
+// chunks of its slice.  When cpw <= 16 the best ring issues the whole range
+// in its first stage (unroll = the smallest power of two >= cpw, 2 stages);
+// for longer ranges a 4-chunk, 2-stage ring beats deeper ones.  Fall back to
+// other rings, then the LDS variants, when the build has no such
+// instantiation for this M.
 int pick(int M, int N, int K, int S, lowm_tactic* t) {
   const int rc = check_sizes(M, N, K, S);
   if (rc != LOWM_OK) return rc;
@@ -169,15 +173,6 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
   }
   if (nvec % 32 == 0 && M <= 32) {
     const int pairs = nvec / 32;   // line pairs per wavefront
-    // Measured on MI355X: 32-row line tiles beat 16-row ones only without
-    // split-K, for 5..16 activation rows, 16 line pairs per wavefront and at
-    // least 192 tiles (M 16, N 6144, K 4096: 12.3 vs 14.4 us; M 16, N 24576:
-    // 32.9 vs 40.5); with split_k 2..8, other slice lengths or fewer tiles
-    // they lose.
-    if (S == 1 && M > 4 && M <= 16 && pairs == 16 && (N + 31) / 32 >= 192) {
-      t->rows = 32;
-      if (provides({kStageLine, 2, 2})) return LOWM_OK;
-    }
     if (!(M > 16 && pairs >= 16)) {
       const int ring = (M <= 4 && pairs >= 8 && pairs < 16) ? 4 : 2;
       t->rows = 16;

@@ -22,7 +22,7 @@ CASES = [
     (4, [1024, 2048], 1024, 1),            # split_k 1: no workspace
     (1, [6144] * 8, 4096, 8),              # the largest batch
     (4, [768], 4096, 2),                   # a batch of one
-    (8, [6144, 6144], 4096, 1),            # 32-row line tiles for every GEMM
+    (8, [6144, 6144], 4096, 1),            # quarter tiles of 32 rows for every GEMM
     (8, [6144, 1024], 4096, 1),            # quarter tiles, one width for every N
     (24, [6144, 512], 4096, 2),            # quarter tiles: 16 rows for the batch, 64 alone
     (64, [6144, 1024], 4096, 1),           # quarter tiles: 16 rows for the batch, 32 alone
