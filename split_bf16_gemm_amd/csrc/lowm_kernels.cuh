@@ -1422,8 +1422,9 @@ __device__ __forceinline__ void strip_epilogue(const Args& a, f32x4 (&acc)[MB], 
   // a5/a6: the owner folds its strip in rank order (its own partial from
   // registers), stores C and returns every slot and the counter to zero.
   // The peers' slots of BPC blocks of 4 rows per lane are loaded at once
-  // (all blocks for split_k 2, two for 3 and 4, one above), so the fold
-  // waits for one round trip per group, not per block.  Rows >= M fold row 0
+  // (all blocks for split_k 2..4, one at a time above: two at split_k 8
+  // measured 0.2-0.4 us slower), so the fold waits for one round trip per
+  // group, not per block.  Rows >= M fold row 0
   // again and keep nothing.
   LOWM_STALL(kSiteFold, 0);
   LOWM_OWNER_FENCE();
@@ -1451,7 +1452,7 @@ __device__ __forceinline__ void strip_epilogue(const Args& a, f32x4 (&acc)[MB], 
   };
   auto fold_all = [&](auto sn_c) {
     constexpr int SN = decltype(sn_c)::value;
-    constexpr int BPC0 = SN == 2 ? MB : (SN == 3 || SN == 4) ? 2 : 1;
+    constexpr int BPC0 = (SN == 2 || SN == 3 || SN == 4) ? MB : 1;
     constexpr int BPC = BPC0 < MB ? BPC0 : MB;
 #pragma unroll
     for (int b0 = 0; b0 + BPC <= MB; b0 += BPC)
