@@ -21,13 +21,20 @@
 //      LINE   W global -> LDS in whole 128-byte lines (non-temporal
 //             direct-to-LDS loads) into a ring private to each wavefront;
 //             the wavefronts split the K slice; activation operands straight
-//             from memory into registers.  The default for M <= 16.
+//             from memory into registers.  The default for M <= 4 with
+//             split-K.
+//      QUARTER each wavefront one quarter of the K slice for the whole tile,
+//             weight and activation rows alike through its own LDS ring with
+//             the same whole-line loads; the quarter sums are added in order
+//             through LDS and each wavefront then owns 16 output columns.
+//             The default without split-K and for 5..32 rows with it (as
+//             the host's tactic rules state).
 //      PANEL  64-row tiles, each wavefront owning 16 of them for the whole K
 //             slice; W as in LINE, and the activation panel of each 64-K
 //             step loaded once per workgroup into an LDS ring that all four
 //             wavefronts read, refilled only after a workgroup barrier.
 //             Each wavefront then owns its 16 output columns through the
-//             exchange as well.  The default for M > 16.
+//             exchange as well.  The default above 32 rows with split-K.
 //      REG    W global -> a register ring per wavefront (any K slice).
 //      LDS    W global -> an LDS ring of NS stages shared by the workgroup,
 //             a stage refilled only after a workgroup barrier that every
@@ -54,9 +61,11 @@
 //    ("agent") scope, the one that spans all XCDs.  No workgroup waits for
 //    another without a bound.
 //
-// Built twice: liblowm.so, and liblowm_stress.so with -DLOWM_STRESS, which
-// adds bounded s_sleep stalls at chosen sites, ranks, wavefronts and tiles
-// (the stall-injection method of the PR's Hardware verification).
+// Built as liblowm.so; as liblowm_stress.so with -DLOWM_STRESS, which adds
+// bounded s_sleep stalls at chosen sites, ranks, wavefronts and tiles (the
+// stall-injection method of the PR's Hardware verification); and, when asked
+// for, as liblowm_fenced.so with -DLOWM_FENCED, a comparison build whose
+// exchange uses a release arrival and an acquire fence.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -121,8 +121,9 @@ constexpr Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-// Rows per tile the build provides: 16 * RG for RG in kRowGroups (the panel
-// tiles are 64 rows: 16 per wavefront).
+// Rows per tile the build provides: 16 * RG for RG in kRowGroups (line-pair,
+// register and LDS tiles 16 or 32; quarter tiles 16, 32 or 64; panel tiles 64
+// with 16 per wavefront, or 32 with 16 per pair of wavefronts).
 constexpr int kRowGroups[] = {1, 2, 4};
 constexpr int kNumRowGroups = sizeof(kRowGroups) / sizeof(kRowGroups[0]);
 constexpr int rg_index(int rg) {
