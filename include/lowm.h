@@ -13,9 +13,10 @@
  * partials, always in rank order 0, 1, ..., split_k-1, then rounds once to
  * bf16 (round-to-nearest-even) and is the only writer of C.  The owner is the
  * last rank of the tile to arrive (a per-tile counter in the workspace), or,
- * for split_k 2..4 and tiles of M x (tile rows) <= 64 elements (M <= 4 with
- * the default 16-row tiles), the tile's last rank when it finds every peer's
- * partial already in the workspace.  That rank polls for at most 20 us
+ * for split_k 2..4 and line-pair, register or LDS tiles of M x (tile rows)
+ * <= 64 elements (M <= 4 with the 16-row line-pair tiles that are the default
+ * there), the tile's last rank when it finds every peer's partial already in
+ * the workspace.  That rank polls for at most 20 us
  * and then arrives like any other, so no workgroup waits for another without
  * a bound and any grid size completes.
  *

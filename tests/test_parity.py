@@ -164,6 +164,27 @@ def test_workspace_returns_to_zero_and_guard_intact(lib):
     assert (host[need:] == 0xA5).all(), "the kernel wrote past the workspace"
 
 
+def test_workspace_status_reads_the_counter_lines(lib):
+    """lowm_workspace_status counts the tiles whose fault word (word 1 of
+    their 256-byte counter line) or arrival count (word 0) is non-zero; the
+    words are planted from the host, then a launch on a clean workspace
+    leaves both counts at zero."""
+    dev = device()
+    wl = workloads.HEADLINE
+    ws = lib.make_workspace(wl.M, wl.N, wl.K, wl.split_k, dev)
+    words = ws.view(torch.int32)
+    words[64 * 3 + 1] = 1          # tile 3: fault word
+    words[64 * 5] = 1              # tile 5: open arrival count
+    words[64 * 7 + 1] = 1          # tile 7: both
+    words[64 * 7] = 2
+    assert lib.workspace_status(ws, wl.N) == (2, 2)
+    ws.zero_()
+    A, W = inputs(wl)
+    say("status after a launch")
+    run(lib, A, W, wl.split_k, workspace=ws)
+    assert lib.workspace_status(ws, wl.N) == (0, 0)
+
+
 def test_split_one_needs_no_workspace(lib):
     wl = workloads.Workload("s1", 4, 640, 1024, 1, seed_a=1, seed_w=2)
     A, W = inputs(wl)
