@@ -116,10 +116,14 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
   // tile, both operands through its own LDS ring).  Measured on MI355X
   // (bench.py --tactic-matrix) at M 1..64, N 1536..24576, K 4096..16384,
   // split_k 1..8 against the line-pair and panel tiles:
-  //   - split_k 1, M <= 32: 32-row tiles, ring 3 (16-row tiles where that
-  //     still gives no more than 192 workgroups): M 16, N 6144, K 4096
+  //   - split_k 1, M <= 32: 32-row tiles (16-row tiles above 16 rows where
+  //     that still gives no more than 192 workgroups): M 16, N 6144, K 4096
   //     10.9 us against 12.3 (line pairs), M 32 12.9 against 13.8 (panel),
-  //     M 4 10.1 against 10.5, M 16 N 24576 32.0 against 33.4;
+  //     M 4 10.1 against 10.5, M 16 N 24576 32.0 against 33.4.  Ring 4 where
+  //     every workgroup fits on the device at once (at most 256 32-row
+  //     workgroups up to 16 rows, where ring 3 would fit two per CU; always
+  //     above, where both fit one): M 1 / 4 / 8 / 32, N 6144 9.61 / 9.80 /
+  //     10.01 / 12.83 us against 9.86 / 10.00 / 10.18 / 12.96 with ring 3;
   //   - split_k >= 2, 4 < M <= 16: the tile width and ring by the number of
   //     32-row workgroups W: <= 96 rows 16 ring 3, <= 192 rows 32 ring 3,
   //     <= 384 rows 16 ring 2, else rows 32 ring 2 (M 16 N 6144 split_k 2 /
@@ -146,14 +150,15 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
       return provides({kStageQuarter, 2, ring});
     };
     if (M <= 16 && S == 1) {
-      if (quarter(32, 3)) return LOWM_OK;
+      if ((w32 <= 256 && quarter(32, 4)) || quarter(32, 3)) return LOWM_OK;
     } else if (M > 4 && M <= 16) {
       if (w32 <= 96 ? quarter(16, 3)
                     : w32 <= 192 ? quarter(32, 3) : w32 <= 384 ? quarter(16, 2) : quarter(32, 2))
         return LOWM_OK;
     } else if (M > 16 && S == 1) {
       if (w16 <= 192 ? quarter(16, 3)
-                     : (M <= 32 || w32 <= 384) ? quarter(32, 3) : quarter(64, 2))
+                     : M <= 32 ? (quarter(32, 4) || quarter(32, 3))
+                               : w32 <= 384 ? quarter(32, 3) : quarter(64, 2))
         return LOWM_OK;
     } else if (M > 16 && M <= 32 && S == 2) {
       if (w16 <= 192 ? quarter(16, 3) : quarter(64, 3)) return LOWM_OK;

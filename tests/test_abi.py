@@ -130,17 +130,18 @@ def test_pick_panel_tiles_above_32_rows_with_split_or_split_k_4(lib):
 def test_pick_quarter_tiles_where_measured_faster(lib):
     """Quarter tiles: split_k 1 for every M; 5..16 rows with any split_k;
     17..32 rows with split_k 2.  The tile width and ring follow the number
-    of workgroups."""
+    of workgroups and rows."""
     quarter = binding.LOWM_STAGE_QUARTER
     for M, N, K, S, rows, ring in [
-            (16, 6144, 4096, 1, 32, 3), (8, 6144, 4096, 1, 32, 3), (1, 6144, 4096, 1, 32, 3),
-            (4, 24576, 4096, 1, 32, 3),
+            (16, 6144, 4096, 1, 32, 4), (8, 6144, 4096, 1, 32, 4), (1, 6144, 4096, 1, 32, 4),
+            (4, 8192, 4096, 1, 32, 4),       # 256 32-row workgroups: ring 4
+            (4, 24576, 4096, 1, 32, 3),      # 768: ring 3 fits two per CU
             (8, 6144, 4096, 2, 16, 2),       # 384 32-row workgroups
             (16, 6144, 4096, 4, 32, 2),      # 768
             (16, 1536, 8192, 2, 16, 3),      # 96
             (8, 1536, 8192, 4, 32, 3),       # 192
             (12, 6144, 4096, 8, 32, 2),      # 1536
-            (32, 6144, 4096, 1, 32, 3),      # 384 16-row workgroups
+            (32, 6144, 4096, 1, 32, 4),      # 384 16-row workgroups
             (24, 6144, 4096, 2, 64, 3),
             (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
             (20, 3072, 4096, 1, 16, 3),
@@ -148,7 +149,7 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (64, 12288, 4096, 1, 32, 3),     # 384
             (48, 24576, 4096, 1, 64, 2),     # 768
             (64, 2304, 12288, 1, 16, 3),     # 144 16-row workgroups
-            (32, 24576, 4096, 1, 32, 3),     # up to 32 rows: 32-row tiles
+            (32, 24576, 4096, 1, 32, 4),     # up to 32 rows: 32-row tiles
             (48, 100, 512, 1, 16, 3)]:
         t = lib.pick_tactic(M, N, K, S)
         assert (t.stage, t.rows, t.unroll, t.stages) == (quarter, rows, 2, ring), (M, N, K, S, t)
