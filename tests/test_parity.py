@@ -116,6 +116,22 @@ def test_ragged(lib, M, N, K, S):
     check_random(lib, wl)
 
 
+# The largest split_k the boundary accepts (one 16-byte vector of K per rank
+# at K 2048: 256 ranks per tile on the generic fold) and a long K at split_k
+# 64, from one activation row to the largest M.
+LARGEST_SPLIT = [
+    (1, 64, 2048, sbg.binding.MAX_SPLIT_K), (4, 300, 2048, sbg.binding.MAX_SPLIT_K),
+    (64, 100, 4096, sbg.binding.MAX_SPLIT_K), (16, 1000, 16384, 64),
+]
+
+
+@pytest.mark.parametrize("M,N,K,S", LARGEST_SPLIT)
+def test_largest_split_k(lib, M, N, K, S):
+    wl = workloads.Workload(f"split{S}_{M}_{N}_{K}", M, N, K, S,
+                            seed_a=M + 1100, seed_w=N + K)
+    check_random(lib, wl)
+
+
 def test_every_tactic_random(lib):
     """M 20 (two row blocks) with whole 256-K slices: every tactic family
     applies (5 register/LDS variants at 16 rows, 4 at 32, 3 line-pair rings,
