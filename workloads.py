@@ -71,6 +71,22 @@ def make_inputs(wl: Workload):
     return A.contiguous(), W.contiguous()
 
 
+def make_large_w(N: int, K: int, seed: int, device) -> torch.Tensor:
+    """W [N, K] drawn on `device` for operands too large to draw on the host:
+    N(0, 0.02) in fp32 from a seeded torch generator on that device, cast to
+    bf16 with round-to-nearest-even, 8192 rows at a time.  The values differ
+    from a host draw of the same seed; a test copies the rows it judges back
+    to the host for the oracle."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    W = torch.empty((N, K), dtype=torch.bfloat16, device=device)
+    for r0 in range(0, N, 8192):
+        r1 = min(N, r0 + 8192)
+        W[r0:r1] = (torch.randn((r1 - r0, K), generator=g, device=device,
+                                dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    return W
+
+
 def bits(t: torch.Tensor):
     """The uint16 bit patterns of a CPU bf16 tensor, as a numpy array."""
     import numpy as np
