@@ -58,7 +58,7 @@ QUARTER_RINGS = (2, 3, 4)
 
 
 def all_tactics(M: int):
-    """Every tactic this build may provide for M activation rows (the
+    """Every tactic the library may provide for M activation rows (the
     launch returns LOWM_ERR_UNSUPPORTED for those it lacks)."""
     out = []
     for rows in (16, 32):
