@@ -160,11 +160,11 @@ const char* lowm_strerror(int code);
  * none); the cause behind LOWM_ERR_LAUNCH. */
 int lowm_last_hip_error(void);
 
-/* Status of a split-K workspace (the failure detection of the survey's
- * auxiliary subsystems; the pages' own defects were lost or stale reads,
- * PR "Fix two synchronization gaps in the MiniMax M3 low-M split-K GEMM",
- * Description items 1 and 2).  Each 256-byte counter line of the workspace
- * holds, in word 0, the tile's arrival count and, in word 1, its fault word.
+/* Status of a split-K workspace: failure detection for the exchange (the
+ * defects of PR "Fix two synchronization gaps in the MiniMax M3 low-M
+ * split-K GEMM", Description items 1 and 2, were lost or stale reads).
+ * Each 256-byte counter line of the workspace holds, in word 0, the tile's
+ * arrival count and, in word 1, its fault word.
  * An owner that still finds a peer's partial slot unpublished 1 ms after
  * every peer has arrived stops waiting, folds the slot as it reads it and
  * sets the fault word; the library never clears a fault word.  That
@@ -261,13 +261,14 @@ int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out);
  * table of the fastest split_k measured on MI355X (bench.py --split-sweep)
  * over M 4, 8, 16, 32 and 64, N 768 .. 24576, K 2048 .. 16384 (nearest
  * grid point in log2 N and log2 K, the row of the next measured M at or
- * above M), reduced to a power of two that K allows.  Any split_k is correct; this one minimises time per call.  (The
- * PR ships split_k 1 and 2, Hardware verification.)  Returns LOWM_OK, or the
- * error code a launch would return for M, N, K. */
+ * above M), reduced to a power of two that K allows.  Any split_k is
+ * correct; this one minimises time per call.  (The PR ships split_k 1 and 2,
+ * Hardware verification.)  Returns LOWM_OK, or the error code a launch would
+ * return for M, N, K. */
 int lowm_pick_split_k(int M, int N, int K, int* split_k);
 
 /* Host-only: LOWM_OK if a launch with these sizes, output type (f32out != 0:
- * fp32) and tactic (NULL: the default) would find a kernel in this build, else
+ * fp32) and tactic (NULL: the default) would find a kernel in the library, else
  * the error code the launch would return for them (the host-side checks of
  * lowm_gemm_splitk, including the PR's non-empty K loop of Description
  * item 1).  No HIP call is made. */
@@ -276,7 +277,7 @@ int lowm_check_launch(int M, int N, int K, int split_k, int f32out,
 
 /* lowm_gemm_splitk / _f32out with an explicit tactic (NULL: the default),
  * the same product (PR, Description item 2) in another summation order.
- * LOWM_ERR_UNSUPPORTED for a tactic this build does not provide. */
+ * LOWM_ERR_UNSUPPORTED for a tactic the library does not provide. */
 int lowm_gemm_splitk_ex(const void* A, const void* W, void* C,
                         int M, int N, int K, int split_k,
                         void* workspace, void* stream, const lowm_tactic* tactic);

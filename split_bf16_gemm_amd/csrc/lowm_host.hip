@@ -285,7 +285,8 @@ size_t workspace_bytes(int M, int N, int K, int S) {
   // counters for up to ceil(N/16) tiles, then [tiles][split_k][M][BN] fp32
   // partials; tiles * BN never exceeds N rounded up to 64, a multiple of
   // every tile width.  Both parts are multiples of 256 bytes.
-  return counter_bytes(N) + (size_t)S * (size_t)M * round_up((size_t)N, kPartialPad) * sizeof(float);
+  return counter_bytes(N) +
+         (size_t)S * (size_t)M * round_up((size_t)N, kPartialPad) * sizeof(float);
 }
 
 // The push epilogue of a single-GEMM launch (bf16 output).
@@ -641,7 +642,7 @@ const char* lowm_strerror(int code) {
     case LOWM_ERR_INVALID_ARG: return "invalid argument (NULL operand, size <= 0, split_k < 1)";
     case LOWM_ERR_UNSUPPORTED:
       return "unsupported (M > 64, K not a multiple of 8*split_k, split_k > 256, misaligned "
-             "pointer, or tactic not in this build)";
+             "pointer, or a tactic the library does not provide)";
     case LOWM_ERR_WORKSPACE: return "split_k > 1 needs a workspace";
     case LOWM_ERR_LAUNCH: return "a HIP call failed (see lowm_last_hip_error)";
     case LOWM_ERR_SCRATCH:

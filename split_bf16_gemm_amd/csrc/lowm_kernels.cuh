@@ -577,7 +577,8 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   const bool probing = early_probe(a, BN) && rank == a.S - 1;
   if (wave == 0 && probing && !probed) {
 #pragma unroll
-    for (int i = 0; i < kProbeRanks; ++i) probe[i] = load_slot(probe_src(a, E, tile, lane, i, true));
+    for (int i = 0; i < kProbeRanks; ++i)
+      probe[i] = load_slot(probe_src(a, E, tile, lane, i, true));
   }
   auto probe_seen = [&](int i) { return i >= a.S - 1 || lane >= E || probe[i] != 0u; };
 
@@ -683,7 +684,8 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   // elsewhere).
   const bool late = LOWM_LATE_PUBLISH();
   if (!late)
-    for (int e = lane; e < E; e += kWave) store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
+    for (int e = lane; e < E; e += kWave)
+      store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
   pin_issue();
   uint32_t before = 0;
   if (lane == 0)
@@ -692,7 +694,8 @@ __device__ __forceinline__ void workgroup_epilogue(const Args& a, const f32x4 (&
   LOWM_TRACE(kTraceArrived);
   if (late) {   // stress build only: the partial lands after the arrival
     if (before != (uint32_t)(a.S - 1)) LOWM_LATE_STALL();
-    for (int e = lane; e < E; e += kWave) store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
+    for (int e = lane; e < E; e += kWave)
+      store_slot(slots + (size_t)rank * E + e, enc_partial(rank_sum(e)));
   }
   if (before != (uint32_t)(a.S - 1)) {   // not the last rank: done
     LOWM_TRACE(kTraceEnd);
@@ -791,7 +794,9 @@ __device__ __forceinline__ void kernel_body(const Args& a) {
   // loads it issues back to back cover its 16 rows x U*64 contiguous bytes.
   const int nunits = kLds ? (nvec + 63) / 64 : (nvec + 3) / 4;
   const int rot = kLds ? (int)(((unsigned)tile * 5u) % (unsigned)nunits) : 0;
-  auto phys = [&](int u) { return u < nunits ? (u + rot < nunits ? u + rot : u + rot - nunits) : -1; };
+  auto phys = [&](int u) {
+    return u < nunits ? (u + rot < nunits ? u + rot : u + rot - nunits) : -1;
+  };
   const bool whole = kLds ? (nvec % 64 == 0) : (nvec % 4 == 0);
   const int cpw = (nunits + kWaves - 1) / kWaves;            // REG: chunks per wavefront
   const int nsteps = kLds ? nunits : (cpw + U - 1) / U;
@@ -1201,7 +1206,8 @@ __device__ __forceinline__ void line_tile_body(const Args& a, u32x4* __restrict_
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) wv[c * RG + rg] = lds_read_opaque(slot + rg * 2 * kPP + rpos[c]);
+      for (int rg = 0; rg < RG; ++rg)
+        wv[c * RG + rg] = lds_read_opaque(slot + rg * 2 * kPP + rpos[c]);
     lds_wait(wv);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -1665,7 +1671,9 @@ __device__ __forceinline__ void panel_tile_body(const Args& a, u32x4* __restrict
     // the barrier) and are added to the first's, in that order; the first
     // half's wavefront carries on alone.
     float* red = reinterpret_cast<float*>(ring);
-    auto red_at = [&](int b, int i) -> float& { return red[((wn * MB + b) * 4 + i) * kWave + lane]; };
+    auto red_at = [&](int b, int i) -> float& {
+      return red[((wn * MB + b) * 4 + i) * kWave + lane];
+    };
     barrier_keep_loads();
     if (kh == 1) {
 #pragma unroll
@@ -1879,7 +1887,8 @@ __device__ __forceinline__ void quarter_tile_body(const Args& a, u32x4* __restri
     for (int i = 0; i < 4; ++i) {
       float v = red[((wave * MB + b) * 4 + i) * kWave + lane];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) v += red[(((w * NB + wave) * MB + b) * 4 + i) * kWave + lane];
+      for (int w = 1; w < kWaves; ++w)
+        v += red[(((w * NB + wave) * MB + b) * 4 + i) * kWave + lane];
       sum[b][i] = v;
     }
   LOWM_TRACE(kTraceReduced);
@@ -1947,8 +1956,9 @@ void fill_row(KernelFn* row, std::integer_sequence<int, VI...>) {
 template <typename OutT, int MB, int RG>
 void fill_one(Table& t, int out) {
   constexpr int ri = rg_index(RG);
-  fill_row<MB, RG, 0, OutT>(t.fn[out][0][MB - 1][ri], std::make_integer_sequence<int, kNumVariants>{});
-  fill_row<MB, RG, 1, OutT>(t.fn[out][1][MB - 1][ri], std::make_integer_sequence<int, kNumVariants>{});
+  constexpr auto vis = std::make_integer_sequence<int, kNumVariants>{};
+  fill_row<MB, RG, 0, OutT>(t.fn[out][0][MB - 1][ri], vis);
+  fill_row<MB, RG, 1, OutT>(t.fn[out][1][MB - 1][ri], vis);
 }
 template <typename OutT, int MB>
 void fill_mb(Table& t, int out) {
