@@ -22,6 +22,8 @@
  *
  * Layouts: A, W and C are dense row-major with no padding: element (m, k) of A
  * at A + m*K + k, (n, k) of W at W + n*K + k, (m, n) of C at C + m*N + n.
+ * C must not overlap A, W or the workspace (A and W may overlap: they are
+ * only read); a launch given overlapping buffers returns LOWM_ERR_INVALID_ARG.
  *
  * Ownership: the caller owns every buffer.  The library allocates nothing,
  * frees nothing and keeps no mutable global state (a per-device table of
@@ -59,7 +61,9 @@ extern "C" {
 #endif
 
 #define LOWM_OK 0
-/* A NULL operand pointer, M, N or K <= 0, or split_k < 1. */
+/* A NULL operand pointer, M, N or K <= 0, split_k < 1, or an output C whose
+ * bytes overlap A, W, another output of the launch or the workspace (or a
+ * workspace that overlaps A or W). */
 #define LOWM_ERR_INVALID_ARG (-1)
 /* Outside what the kernels support: M > 64 (the low-M regime); K not a
  * multiple of 8 * split_k (every rank's slice must be a non-empty whole number

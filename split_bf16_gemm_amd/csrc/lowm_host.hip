@@ -305,6 +305,10 @@ inline void byte_span(const void* p, int rows, int cols, int ld, size_t elem, ui
   *hi = *lo + ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * elem;
 }
 
+bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < b1 && b0 < a1;
+}
+
 int check_push(const PushSpec& p, const void* C, int M, int N) {
   if (!p.dst || !p.flags || p.value == 0 || p.ld < N) return LOWM_ERR_INVALID_ARG;
   if (((uintptr_t)p.dst & 1) || ((uintptr_t)p.flags & 3)) return LOWM_ERR_UNSUPPORTED;
@@ -312,11 +316,43 @@ int check_push(const PushSpec& p, const void* C, int M, int N) {
   byte_span(C, M, N, N, 2, &c0, &c1);
   byte_span(p.dst, M, N, p.ld, 2, &d0, &d1);
   byte_span(p.flags, 1, (N + 15) / 16, 0, 4, &f0, &f1);
-  auto overlap = [](uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
-    return a0 < b1 && b0 < a1;
-  };
   if (overlap(c0, c1, d0, d1) || overlap(c0, c1, f0, f1) || overlap(d0, d1, f0, f1))
     return LOWM_ERR_INVALID_ARG;
+  return LOWM_OK;
+}
+
+// Outputs the launch writes must not overlap anything it reads or writes
+// besides themselves: no C_g may overlap any A, W or other C of the launch,
+// nor the workspace, and the workspace may overlap no operand.  (Inputs may
+// be shared or overlap each other: they are only read.)
+int check_overlaps(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int K, int S,
+                   const void* workspace) {
+  const size_t celem = f32out ? 4 : 2;
+  uintptr_t w0 = 0, w1 = 0;
+  if (S > 1) {
+    size_t ws = 0;
+    for (int g = 0; g < count; ++g) ws += workspace_bytes(M, gemms[g].N, K, S);
+    w0 = (uintptr_t)workspace;
+    w1 = w0 + ws;
+  }
+  for (int g = 0; g < count; ++g) {
+    uintptr_t c0, c1;
+    byte_span(gemms[g].C, M, gemms[g].N, gemms[g].N, celem, &c0, &c1);
+    if (S > 1 && overlap(c0, c1, w0, w1)) return LOWM_ERR_INVALID_ARG;
+    for (int h = 0; h < count; ++h) {
+      uintptr_t a0, a1, b0, b1;
+      byte_span(gemms[h].A, M, K, K, 2, &a0, &a1);
+      byte_span(gemms[h].W, gemms[h].N, K, K, 2, &b0, &b1);
+      if (overlap(c0, c1, a0, a1) || overlap(c0, c1, b0, b1)) return LOWM_ERR_INVALID_ARG;
+      if (S > 1 && g == 0 && (overlap(w0, w1, a0, a1) || overlap(w0, w1, b0, b1)))
+        return LOWM_ERR_INVALID_ARG;
+      if (h != g) {
+        uintptr_t d0, d1;
+        byte_span(gemms[h].C, M, gemms[h].N, gemms[h].N, celem, &d0, &d1);
+        if (overlap(c0, c1, d0, d1)) return LOWM_ERR_INVALID_ARG;
+      }
+    }
+  }
   return LOWM_OK;
 }
 
@@ -343,6 +379,8 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     if ((uintptr_t)gemms[g].C & (f32out ? 3 : 1)) return LOWM_ERR_UNSUPPORTED;
   }
   if (S > 1 && ((uintptr_t)workspace & 15)) return LOWM_ERR_UNSUPPORTED;
+  rc = check_overlaps(gemms, count, f32out, M, K, S, workspace);
+  if (rc != LOWM_OK) return rc;
   if (push) {
     rc = check_push(*push, gemms[0].C, M, gemms[0].N);
     if (rc != LOWM_OK) return rc;
@@ -639,7 +677,9 @@ int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out) {
 const char* lowm_strerror(int code) {
   switch (code) {
     case LOWM_OK: return "success";
-    case LOWM_ERR_INVALID_ARG: return "invalid argument (NULL operand, size <= 0, split_k < 1)";
+    case LOWM_ERR_INVALID_ARG:
+      return "invalid argument (NULL operand, size <= 0, split_k < 1, or an output that "
+             "overlaps an operand, another output or the workspace)";
     case LOWM_ERR_UNSUPPORTED:
       return "unsupported (M > 64, K not a multiple of 8*split_k, split_k > 256, misaligned "
              "pointer, or a tactic the library does not provide)";

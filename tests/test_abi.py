@@ -20,6 +20,9 @@ HEADER = ROOT / "include" / "lowm.h"
 
 FAKE = 0x10000      # 16-byte aligned, never dereferenced
 FAKE_ODD = 0x10002  # 2-byte aligned only
+# Disjoint fake buffers for calls that must get past the host's overlap check
+# (16 MiB apart: far beyond any span these tests describe).
+FAKE_A, FAKE_W, FAKE_C, FAKE_WS = 0x1000000, 0x2000000, 0x3000000, 0x4000000
 
 
 def declared_functions():
@@ -161,7 +164,8 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
         assert lib.pick_tactic(M, N, K, S).stage != quarter, (M, N, K, S)
 
 
-def call(lib, A=FAKE, W=FAKE, C=FAKE, M=4, N=64, K=256, S=2, ws=FAKE, f32=False, tac=None):
+def call(lib, A=FAKE_A, W=FAKE_W, C=FAKE_C, M=4, N=64, K=256, S=2, ws=FAKE_WS, f32=False,
+         tac=None):
     return lib.call_raw(A, W, C, M, N, K, S, ws, 0, f32out=f32, tactic=tac)
 
 
@@ -181,14 +185,33 @@ def test_unsupported(lib, f32):
     assert call(lib, M=65, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
     assert call(lib, K=260, f32=f32) == binding.LOWM_ERR_UNSUPPORTED       # K % 16 != 0
     assert call(lib, S=257, K=8 * 257, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
-    assert call(lib, A=FAKE + 8, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
-    assert call(lib, W=FAKE + 4, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
-    assert call(lib, ws=FAKE + 8, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
-    assert call(lib, C=FAKE_ODD + 1, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, A=FAKE_A + 8, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, W=FAKE_W + 4, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, ws=FAKE_WS + 8, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, C=FAKE_C + 1, f32=f32) == binding.LOWM_ERR_UNSUPPORTED
 
 
 def test_fp32_output_needs_4_byte_alignment(lib):
-    assert call(lib, C=FAKE_ODD, f32=True) == binding.LOWM_ERR_UNSUPPORTED
+    assert call(lib, C=FAKE_C + 2, f32=True) == binding.LOWM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_overlapping_buffers_are_rejected(lib, f32):
+    """An output whose bytes meet an operand, another output or the
+    workspace (or a workspace that meets an operand) is an invalid argument,
+    found on the host before any HIP call.  M 4, N 64, K 256: A spans 2 KiB,
+    W 32 KiB, C 512 B (bf16) or 1 KiB (fp32)."""
+    E = binding
+    c_bytes = 4 * 64 * (4 if f32 else 2)
+    assert call(lib, C=FAKE_A, f32=f32) == E.LOWM_ERR_INVALID_ARG
+    assert call(lib, C=FAKE_A + 2048 - 4, f32=f32) == E.LOWM_ERR_INVALID_ARG     # A's last bytes
+    assert call(lib, C=FAKE_W - c_bytes + 4, f32=f32) == E.LOWM_ERR_INVALID_ARG  # W's first bytes
+    assert call(lib, C=FAKE_W + 32768 - 4, f32=f32) == E.LOWM_ERR_INVALID_ARG    # W's last bytes
+    assert call(lib, C=FAKE_WS, f32=f32) == E.LOWM_ERR_INVALID_ARG
+    assert call(lib, ws=FAKE_A, f32=f32) == E.LOWM_ERR_INVALID_ARG
+    assert call(lib, ws=FAKE_W + 16, f32=f32) == E.LOWM_ERR_INVALID_ARG
+    assert call(lib, ws=FAKE_C - 16, f32=f32) == E.LOWM_ERR_INVALID_ARG          # runs into C
+    assert lib.lib.lowm_last_hip_error() == 0
 
 
 def test_workspace_required_for_split(lib):
@@ -285,14 +308,14 @@ def test_pick_split_k(lib):
     assert lib.lib.lowm_pick_split_k(4, 64, 256, None) == binding.LOWM_ERR_INVALID_ARG
 
 
-def batch_call(lib, descs, count=None, M=4, K=256, S=2, ws=FAKE):
+def batch_call(lib, descs, count=None, M=4, K=256, S=2, ws=FAKE_WS):
     n = len(descs) if count is None else count
     arr = (binding.GemmDesc * max(1, len(descs)))(*descs)
     return lib.lib.lowm_gemm_splitk_batched(arr if descs else None, n, M, K, S, ws, None)
 
 
 def test_batched_validation(lib):
-    d = binding.GemmDesc(FAKE, FAKE, FAKE, 64)
+    d = binding.GemmDesc(FAKE_A, FAKE_W, FAKE_C, 64)
     assert batch_call(lib, [], count=0) == binding.LOWM_ERR_INVALID_ARG
     assert batch_call(lib, [d], count=0) == binding.LOWM_ERR_INVALID_ARG
     assert batch_call(lib, [d] * 9) == binding.LOWM_ERR_UNSUPPORTED
@@ -304,6 +327,25 @@ def test_batched_validation(lib):
     assert batch_call(lib, [d, binding.GemmDesc(FAKE, FAKE, FAKE_ODD + 1, 64)]) == \
         binding.LOWM_ERR_UNSUPPORTED
     assert batch_call(lib, [d, d], ws=0) == binding.LOWM_ERR_WORKSPACE
+    assert lib.lib.lowm_last_hip_error() == 0
+
+
+def test_batched_outputs_must_not_overlap(lib):
+    """Outputs of one launch must not meet each other, any operand of the
+    launch or the workspace; inputs may be shared (they are only read), which
+    the GPU tests exercise."""
+    E = binding
+    G = binding.GemmDesc
+    d0 = G(FAKE_A, FAKE_W, FAKE_C, 64)
+    assert batch_call(lib, [d0, G(FAKE_A, FAKE_W, FAKE_C + 256, 64)]) == E.LOWM_ERR_INVALID_ARG
+    assert batch_call(lib, [d0, G(FAKE_A, FAKE_W + 0x100000, FAKE_W, 64)]) == \
+        E.LOWM_ERR_INVALID_ARG                      # GEMM 1's C over GEMM 0's W
+    assert batch_call(lib, [d0, G(FAKE_A + 0x100000, FAKE_W, FAKE_A, 64)]) == \
+        E.LOWM_ERR_INVALID_ARG                      # GEMM 1's C over GEMM 0's A
+    # the workspace is the two GEMMs' workspaces back to back: GEMM 1's C
+    # just past the first one still meets the second
+    ws0 = lib.workspace_bytes(4, 64, 256, 2)
+    assert batch_call(lib, [d0, G(FAKE_A, FAKE_W, FAKE_WS + ws0, 64)]) == E.LOWM_ERR_INVALID_ARG
     assert lib.lib.lowm_last_hip_error() == 0
 
 
@@ -330,9 +372,9 @@ C_ADDR, PUSH_ADDR, FLAG_ADDR = 0x10000, 0x100000, 0x200000
 
 
 def push_call(lib, push=PUSH_ADDR, ld=64, flags=FLAG_ADDR, value=1, C=C_ADDR, M=4, N=64,
-              K=256, S=2, ws=FAKE):
-    return lib.lib.lowm_gemm_splitk_push(FAKE, FAKE, C, M, N, K, S, ws, push, ld, flags, value,
-                                         None, None)
+              K=256, S=2, ws=FAKE_WS):
+    return lib.lib.lowm_gemm_splitk_push(FAKE_A, FAKE_W, C, M, N, K, S, ws, push, ld, flags,
+                                         value, None, None)
 
 
 def test_push_validation(lib):

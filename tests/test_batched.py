@@ -80,3 +80,51 @@ def test_batch_reuses_its_workspace():
             single = lib.gemm(As[g], Ws[g], S, workspace=lib.make_workspace(4, wl.N, K, S, dev))
             torch.cuda.synchronize()
             assert np.array_equal(to_bits(outs[g]), to_bits(single))
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_batch_may_share_one_activation(S):
+    """Projections of one activation (query, key and value weights): every
+    GEMM of the batch reads the same A, which the launch allows since inputs
+    are only read."""
+    lib = sbg.load()
+    dev = device()
+    M, K, Ns = 4, 4096, [6144, 1024, 1024]
+    wls = batch_workloads(M, Ns, K, S)
+    A = inputs(wls[0])[0].to(dev)
+    Ws = [inputs(wl)[1].to(dev) for wl in wls]
+    ws = None
+    if S > 1:
+        ws = torch.zeros(lib.batched_workspace_bytes(M, Ns, K, S), dtype=torch.uint8,
+                         device=dev)
+    say("batched shared A", M, Ns, K, S)
+    outs = lib.gemm_batched([A] * len(Ws), Ws, S, workspace=ws)
+    torch.cuda.synchronize()
+    for g, wl in enumerate(wls):
+        single = lib.gemm(A, Ws[g], S, workspace=lib.make_workspace(M, Ns[g], K, S, dev))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(outs[g]), to_bits(single)), \
+            f"GEMM {g} over the shared activation differs from its single launch"
+    assert_bf16_launch(lib, A, Ws[0], wls[0], to_bits(outs[0]), what="shared-A GEMM 0")
+    if ws is not None:
+        assert not ws.cpu().numpy().any(), "the shared-A batch left its workspace non-zero"
+
+
+def test_overlapping_outputs_are_refused_before_any_kernel():
+    """Two outputs of one batch on the same memory: the launch returns an
+    invalid-argument error and leaves every buffer as it was."""
+    lib = sbg.load()
+    dev = device()
+    M, K, S, N = 4, 1024, 2, 512
+    wls = batch_workloads(M, [N, N], K, S)
+    As = [inputs(wl)[0].to(dev) for wl in wls]
+    Ws = [inputs(wl)[1].to(dev) for wl in wls]
+    shared = torch.full((M, N), 1.5, dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(lib.batched_workspace_bytes(M, [N, N], K, S), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    say("batched overlapping outputs", M, N, K, S)
+    with pytest.raises(sbg.binding.LowmError, match="overlap"):
+        lib.gemm_batched(As, Ws, S, outs=[shared, shared], workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((shared == 1.5).all()), "a refused launch wrote its output"
+    assert not ws.cpu().numpy().any(), "a refused launch touched the workspace"
