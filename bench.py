@@ -282,11 +282,12 @@ def _counter_medians(run_dir: Path, counter: str) -> dict:
 
 
 def summarize_pmc(wl_name: str, tactic_text, fetch: Path, write: Path, cfetch: Path,
-                  cwrite: Path) -> dict:
+                  cwrite: Path, out: Path = PMC_FILE) -> dict:
     """HBM bytes per launch of the GEMM kernel from four rocprofv3 --pmc runs
     (FETCH_SIZE and WRITE_SIZE of bench.py, then of --calibrate-copy), each
     scaled by what the counter reads for the copy of COPY_BYTES; written to
-    PMC_FILE with the kernel source hash, workload and tactic it belongs to."""
+    `out` (PMC_FILE, the one roofline.traffic reads, unless another is named)
+    with the kernel source hash, workload and tactic it belongs to."""
     import split_bf16_gemm_amd as sbg
     import workloads
     wl = workloads.by_name(wl_name)
@@ -314,7 +315,7 @@ def summarize_pmc(wl_name: str, tactic_text, fetch: Path, write: Path, cfetch: P
            "copy_bytes": COPY_BYTES, "fetch_scale": round(f_scale, 5),
            "write_scale": round(w_scale, 5), "traffic_bytes_per_launch": traffic,
            "algorithmic_bytes_per_launch": algorithmic_bytes(wl.M, wl.N, wl.K, wl.split_k)}
-    PMC_FILE.write_text(json.dumps(rec, indent=1) + "\n")
+    out.write_text(json.dumps(rec, indent=1) + "\n")
     return rec
 
 
@@ -798,6 +799,9 @@ def main():
                     help="no GPU: write the HBM traffic record from four rocprofv3 --pmc "
                          "output directories (FETCH_SIZE, WRITE_SIZE of this bench, then of "
                          "--calibrate-copy)")
+    ap.add_argument("--pmc-file", default=str(PMC_FILE),
+                    help="where --summarize-pmc writes its record (default: the one "
+                         "roofline.traffic reads)")
     ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
                     help="no GPU: print the median per-dispatch value of every counter in "
                          "these rocprofv3 --pmc output directories, per GEMM kernel")
@@ -832,7 +836,8 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        rec = summarize_pmc(args.workload, args.tactic, *(Path(d) for d in args.summarize_pmc))
+        rec = summarize_pmc(args.workload, args.tactic, *(Path(d) for d in args.summarize_pmc),
+                            out=Path(args.pmc_file))
         print(json.dumps(rec), flush=True)
         return
 
