@@ -132,6 +132,27 @@ def test_largest_split_k(lib, M, N, K, S):
     check_random(lib, wl)
 
 
+def _drawn_shapes(n=16, seed=2024):
+    """Shapes drawn from a fixed seed over the whole supported range: M 1..64,
+    N 1..3000 (mostly ragged), split_k 1..16, K a multiple of 8 * split_k up
+    to 4096 (slices that are whole line pairs, whole 64-K steps, or neither)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 65))
+        N = int(rng.integers(1, 3001))
+        S = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 16]))
+        K = 8 * S * int(rng.integers(1, 4096 // (8 * S) + 1))
+        out.append((M, N, K, S))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,S", _drawn_shapes())
+def test_drawn_shapes_default_tactic(lib, M, N, K, S):
+    wl = workloads.Workload(f"drawn_{M}_{N}_{K}_{S}", M, N, K, S, seed_a=M + N, seed_w=K + S)
+    check_random(lib, wl)
+
+
 def test_every_tactic_random(lib):
     """M 20 (two row blocks) with whole 256-K slices: every tactic family
     applies (5 register/LDS variants at 16 rows, 4 at 32, 3 line-pair rings,
