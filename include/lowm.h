@@ -221,9 +221,18 @@ int lowm_workspace_status(const void* workspace, int N, void* stream, int* fault
  *              activation rows) through a ring of `stages` 64-K slots of its
  *              own in LDS, with whole-line direct-to-LDS loads; no barrier in
  *              the main loop; the four quarter sums are added in order
- *              through LDS at the end.  rows 16, 32 or 64, unroll 2, stages
+ *              through LDS at the end.  rows 16, 32, 48 or 64, unroll 2, stages
  *              2, 3 or 4 (where LDS and the wait counter allow); the K slice
  *              a multiple of 256.
+ *              LOWM_STAGE_QUARTER_ROWS: QUARTER tiles whose workgroups each
+ *              take one block of 16 * unroll activation rows (the last block
+ *              may be shorter): ceil(M / (16 * unroll)) workgroups per tile,
+ *              on one XCD, each streaming the tile's W rows (the blocks after
+ *              the first find them in the L2) and only its own activation
+ *              rows.  The same summation order, so the same bits, as
+ *              QUARTER.  rows 16, 32, 48 or 64, unroll 1..4, stages as
+ *              QUARTER; split_k 1 only; not with the push epilogue (every
+ *              block of a tile would raise its flags).
  *              LOWM_STAGE_LDS: W goes global -> an LDS ring of `stages`
  *              stages shared by the workgroup; a stage holds 512 K of each of
  *              the tile's rows, each direct-to-LDS load moving 1 KB of one
@@ -235,7 +244,8 @@ int lowm_workspace_status(const void* workspace, int N, void* stream, int* fault
  *              chunks (4, 8 or 16) per wavefront per stage; each wavefront
  *              streams its own contiguous quarter of the K slice.  stages 2.
  *   rows       W rows (output columns) per workgroup tile: 16 or 32 (LINE,
- *              LDS, REG), 64 or 32 (PANEL), 16, 32 or 64 (QUARTER).
+ *              LDS, REG), 64 or 32 (PANEL), 16, 32, 48 or 64 (QUARTER,
+ *              QUARTER_ROWS).
  *   waves      wavefronts per workgroup: always 4.
  *   unroll     see stage.
  *   stages     ring depth, see stage.
@@ -247,6 +257,7 @@ int lowm_workspace_status(const void* workspace, int N, void* stream, int* fault
 #define LOWM_STAGE_LINE 3
 #define LOWM_STAGE_PANEL 4
 #define LOWM_STAGE_QUARTER 5
+#define LOWM_STAGE_QUARTER_ROWS 6
 typedef struct lowm_tactic {
     int stage;
     int rows;
@@ -257,6 +268,9 @@ typedef struct lowm_tactic {
 
 /* The tactic lowm_gemm_splitk would use for these sizes (written to *out).
  * Returns LOWM_OK or an error code for sizes it would reject.  Host-only.
+ * (The push entry point picks the same way but never takes
+ * LOWM_STAGE_QUARTER_ROWS: it uses the QUARTER or PANEL tiles the rules give
+ * without that family.)
  * (The PR ships one fixed tactic per split_k, Hardware verification; this
  * one is chosen per shape from measurements on MI355X.) */
 int lowm_pick_tactic(int M, int N, int K, int split_k, lowm_tactic* out);

@@ -26,6 +26,7 @@ LOWM_STAGE_REG = 1
 LOWM_STAGE_LINE = 3
 LOWM_STAGE_PANEL = 4
 LOWM_STAGE_QUARTER = 5
+LOWM_STAGE_QUARTER_ROWS = 6
 MAX_M = 64
 MAX_SPLIT_K = 256
 
@@ -47,15 +48,16 @@ class Tactic(ctypes.Structure):
 
     def __repr__(self) -> str:
         st = {LOWM_STAGE_LDS: "lds", LOWM_STAGE_REG: "reg", LOWM_STAGE_LINE: "line",
-              LOWM_STAGE_PANEL: "panel", LOWM_STAGE_QUARTER: "quarter"}.get(self.stage,
-                                                                          str(self.stage))
+              LOWM_STAGE_PANEL: "panel", LOWM_STAGE_QUARTER: "quarter",
+              LOWM_STAGE_QUARTER_ROWS: "qrows"}.get(self.stage, str(self.stage))
         return (f"Tactic({st}, rows={self.rows}, waves={self.waves}, "
                 f"unroll={self.unroll}, stages={self.stages})")
 
 
 def tactic(stage: str, rows: int, unroll: int, stages: int, waves: int = 4) -> Tactic:
     code = {"lds": LOWM_STAGE_LDS, "reg": LOWM_STAGE_REG, "line": LOWM_STAGE_LINE,
-            "panel": LOWM_STAGE_PANEL, "quarter": LOWM_STAGE_QUARTER}[stage]
+            "panel": LOWM_STAGE_PANEL, "quarter": LOWM_STAGE_QUARTER,
+            "qrows": LOWM_STAGE_QUARTER_ROWS}[stage]
     return Tactic(code, rows, waves, unroll, stages)
 
 

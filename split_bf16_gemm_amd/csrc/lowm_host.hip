@@ -66,8 +66,14 @@ KernelFn lookup(bool f32out, int act, int M, const lowm_tactic& t, bool push = f
 constexpr size_t kActLdsMax = 48 * 1024;
 size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
 
-// Default tactic, in order: quarter tiles where the rules below name them,
-// panel tiles above 16 rows, line-pair tiles, the register ring.
+// The kernel a launch with tactic t runs (defined below).
+KernelFn select_kernel(bool f32out, int M, int S, int nvec, const lowm_tactic& t,
+                       size_t* dyn_lds, bool push = false);
+
+// Default tactic, in order: quarter-rows tiles for 33..64 rows without
+// split-K where their grid fits the device once, quarter tiles where the
+// rules below name them, panel tiles above 16 rows, line-pair tiles, the
+// register ring.
 // Line-pair tiles (the default for M <= 4 with split-K, where the K slice is
 // whole 64-K line pairs per wavefront): 16 rows, a ring of 4 slots for
 // M <= 4 with 8..15 pairs per wavefront and of 2 otherwise.  Measured on
@@ -84,7 +90,7 @@ size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
 // for longer ranges a 4-chunk, 2-stage ring beats deeper ones.  Fall back to
 // other rings, then the LDS variants, when the build has no such
 // instantiation for this M.
-int pick(int M, int N, int K, int S, lowm_tactic* t) {
+int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   const int rc = check_sizes(M, N, K, S);
   if (rc != LOWM_OK) return rc;
   const int nvec = K / S / kVecK;
@@ -149,6 +155,33 @@ int pick(int M, int N, int K, int S, lowm_tactic* t) {
       t->rows = rows;
       return provides({kStageQuarter, 2, ring});
     };
+    // Quarter-rows tiles for 33..64 rows without split-K (not for the push
+    // epilogue): two workgroups per tile, one per 32-row block, and the
+    // narrowest tile width (16..64 columns) at which the blocks fill the 256
+    // CUs once; above that width the rules below.  Measured on MI355X at
+    // M 64, K 4096 against the quarter default: N 2048 / 4096 / 6144 / 8192
+    // 9.3 / 12.2 / 15.4 / 18.4 us against 13.4 / 16.3 / 17.1 / 20.2 (the
+    // activation bytes per CU fall from 512 KB to 256 KB); M 40 / 48 / 56 at
+    // N 6144 and M 64 at K 8192 and 16384 gain as well.  Same summation
+    // order, so the same bits, as the quarter tiles.
+    if (M > 32 && S == 1 && !push) {
+      const long blocks = (M + 31) / 32;
+      for (int nb = 1; nb <= 4; ++nb)
+        if ((long)((N + 16 * nb - 1) / (16 * nb)) * blocks <= 256) {
+          t->rows = 16 * nb;
+          t->stage = kStageQuarterRows;
+          t->unroll = 2;
+          t->stages = nb == 1 ? 4 : 3;
+          t->waves = kWaves;
+          bool ok = true;
+          for (int f = 0; f < 2; ++f) {
+            size_t dyn = 0;
+            ok = ok && select_kernel(f == 1, M, 1, nvec, *t, &dyn) != nullptr;
+          }
+          if (ok) return LOWM_OK;
+          break;
+        }
+    }
     if (M <= 16 && S == 1) {
       if ((w32 <= 256 && quarter(32, 4)) || quarter(32, 3)) return LOWM_OK;
     } else if (M > 4 && M <= 16) {
@@ -262,9 +295,19 @@ int pick_split(int M, int N, int K, int* split_k) {
 // The kernel a launch with tactic t runs: the activation slice is staged in
 // LDS when it is small and whole 1 KB pieces (and the build has that
 // instantiation); otherwise the wavefronts load activation operands from L2.
-KernelFn select_kernel(bool f32out, int M, int nvec, const lowm_tactic& t, size_t* dyn_lds,
-                       bool push = false) {
+KernelFn select_kernel(bool f32out, int M, int S, int nvec, const lowm_tactic& t,
+                       size_t* dyn_lds, bool push) {
   *dyn_lds = 0;
+  // quarter-rows tiles: the quarter kernel of 16*unroll activation rows,
+  // launched with H = ceil(M / (16*unroll)) workgroups per tile (split_k 1;
+  // no push epilogue, whose flags every block of a tile would raise)
+  if (t.stage == kStageQuarterRows) {
+    if (S != 1 || push || t.unroll < 1 || t.unroll > 4 || nvec % 32 != 0) return nullptr;
+    lowm_tactic q = t;
+    q.stage = kStageQuarter;
+    q.unroll = 2;
+    return lookup(f32out, 0, M < 16 * t.unroll ? M : 16 * t.unroll, q);
+  }
   // line-pair tiles stream whole 64-K line pairs per wavefront; panel tiles
   // whole 64-K steps of the slice (of each half of it with 32-row tiles)
   if (t.stage == kStageLine && nvec % 32 != 0) return nullptr;
@@ -394,12 +437,12 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     // (N only sets the tile width and ring, which keep the summation order).
     int n_min = gemms[0].N;
     for (int g = 1; g < count; ++g) n_min = gemms[g].N < n_min ? gemms[g].N : n_min;
-    rc = pick(M, n_min, K, S, &t);
+    rc = pick(M, n_min, K, S, &t, push != nullptr);
     if (rc != LOWM_OK) return rc;
   }
   const int nvec = K / S / kVecK;
   size_t dyn_lds = 0;
-  const KernelFn fn = select_kernel(f32out, M, nvec, t, &dyn_lds, push != nullptr);
+  const KernelFn fn = select_kernel(f32out, M, S, nvec, t, &dyn_lds, push != nullptr);
   if (!fn) return LOWM_ERR_UNSUPPORTED;
 
   const int BN = t.rows;
@@ -417,7 +460,8 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     sl.part = S > 1 ? reinterpret_cast<uint32_t*>(ws + counter_bytes(N)) : nullptr;
     ws_off += workspace_bytes(M, N, K, S);
     const size_t tiles = (size_t)((N + BN - 1) / BN);
-    grid += round_up(tiles, kXcds) * (size_t)S;
+    const size_t blocks = t.stage == kStageQuarterRows ? (M + 16 * t.unroll - 1) / (16 * t.unroll) : 1;
+    grid += round_up(tiles, kXcds) * (size_t)S * blocks;
     if (grid > 0x7fffffffu) return LOWM_ERR_UNSUPPORTED;
     sl.bid_end = (int)grid;
   }
@@ -664,7 +708,7 @@ int lowm_check_launch(int M, int N, int K, int split_k, int f32out, const lowm_t
     if (rc != LOWM_OK) return rc;
   }
   size_t dyn = 0;
-  return lowm::select_kernel(f32out != 0, M, K / split_k / lowm::kVecK, t, &dyn)
+  return lowm::select_kernel(f32out != 0, M, split_k, K / split_k / lowm::kVecK, t, &dyn)
              ? LOWM_OK
              : LOWM_ERR_UNSUPPORTED;
 }

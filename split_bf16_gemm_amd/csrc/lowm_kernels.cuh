@@ -1724,13 +1724,13 @@ struct QuarterShape {
   static constexpr int slot_elems = G * kPP;     // one wavefront's step
   static constexpr int lds_bytes = kWaves * R * slot_elems * 16;
   static constexpr int red_floats = kWaves * NB * MB * 4 * kWave;
-  static constexpr bool valid = MB >= 1 && MB <= 4 && (NB == 1 || NB == 2 || NB == 4) &&
+  static constexpr bool valid = MB >= 1 && MB <= 4 && NB >= 1 && NB <= 4 &&
                                 R >= 2 && R <= 8 && (R - 1) * G <= 63 &&
                                 lds_bytes <= 160 * 1024 && red_floats * 4 <= lds_bytes;
 };
 
 template <int MB, int NB, int R, typename OutT>
-__device__ __forceinline__ void quarter_tile_body(const Args& a, u32x4* __restrict__ lds) {
+__device__ __forceinline__ void quarter_tile_body(const Args& a0, u32x4* __restrict__ lds) {
   using SH = QuarterShape<MB, NB, R>;
   constexpr int BN = SH::BN;
   constexpr int G = SH::G;
@@ -1742,8 +1742,28 @@ __device__ __forceinline__ void quarter_tile_body(const Args& a, u32x4* __restri
   const int g = lane >> 4;
   const int l16 = lane & 15;
 
+  // A launch whose M exceeds the 16*MB rows of the kernel (the quarter-rows
+  // tiles, split_k 1) gives each tile H workgroups, one per block of 16*MB
+  // activation rows; block h is decoded as one more rank of the tile, so the
+  // blocks of a tile share an XCD and the later ones find its W rows in the
+  // L2.  Each block is then a GEMM of its own rows: A and C start at row
+  // 16*MB*h.  With H = 1 (every other launch) nothing changes.
+  const int H = (a0.M + 16 * MB - 1) / (16 * MB);
   int tile, rank;
-  decode_tile(a, BN, false, tile, rank);
+  {
+    Args d = a0;
+    d.S = a0.S * H;
+    decode_tile(d, BN, false, tile, rank);
+  }
+  const int h = rank / a0.S;
+  rank -= h * a0.S;
+  Args a = a0;
+  if (H > 1) {
+    const int m0 = 16 * MB * h;
+    a.A = a0.A + (size_t)m0 * a0.K;
+    a.C = static_cast<typename OutStore<OutT>::type*>(a0.C) + (size_t)m0 * a0.N;
+    a.M = a0.M - m0 < 16 * MB ? a0.M - m0 : 16 * MB;
+  }
   LOWM_TRACE(kTraceEntry);
   LOWM_TRACE_IDS();
   if (tile * BN >= a.N) return;        // a whole workgroup past the end (grid padding)
@@ -1964,6 +1984,7 @@ template <typename OutT, int MB>
 void fill_mb(Table& t, int out) {
   fill_one<OutT, MB, 1>(t, out);
   fill_one<OutT, MB, 2>(t, out);
+  fill_one<OutT, MB, 3>(t, out);
   fill_one<OutT, MB, 4>(t, out);
 }
 // Every kernel of output kind OutT into row `out` of the table.

@@ -27,7 +27,8 @@ enum Stage : int {
   kStageReg = LOWM_STAGE_REG,
   kStageLine = LOWM_STAGE_LINE,
   kStagePanel = LOWM_STAGE_PANEL,
-  kStageQuarter = LOWM_STAGE_QUARTER
+  kStageQuarter = LOWM_STAGE_QUARTER,
+  kStageQuarterRows = LOWM_STAGE_QUARTER_ROWS
 };
 
 // ---------------------------------------------------------------------------
@@ -122,9 +123,9 @@ constexpr Variant kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 // Rows per tile the build provides: 16 * RG for RG in kRowGroups (line-pair,
-// register and LDS tiles 16 or 32; quarter tiles 16, 32 or 64; panel tiles 64
-// with 16 per wavefront, or 32 with 16 per pair of wavefronts).
-constexpr int kRowGroups[] = {1, 2, 4};
+// register and LDS tiles 16 or 32; quarter tiles 16, 32, 48 or 64; panel
+// tiles 64 with 16 per wavefront, or 32 with 16 per pair of wavefronts).
+constexpr int kRowGroups[] = {1, 2, 3, 4};
 constexpr int kNumRowGroups = sizeof(kRowGroups) / sizeof(kRowGroups[0]);
 constexpr int rg_index(int rg) {
   for (int i = 0; i < kNumRowGroups; ++i)

@@ -92,7 +92,7 @@ def test_pick_tactic_is_valid_for_every_workload(lib):
     import workloads
     for wl in workloads.ALL:
         t = lib.pick_tactic(wl.M, wl.N, wl.K, wl.split_k)
-        assert t.rows in (16, 32, 64) and t.waves == 4
+        assert t.rows in (16, 32, 48, 64) and t.waves == 4
         if t.stage in (binding.LOWM_STAGE_REG, binding.LOWM_STAGE_LDS):
             assert t.rows >= min(32, 16 * ((wl.M + 15) // 16))
         assert lib.check_launch(wl.M, wl.N, wl.K, wl.split_k, tactic=t) == 0
@@ -148,12 +148,9 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (24, 6144, 4096, 2, 64, 3),
             (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
             (20, 3072, 4096, 1, 16, 3),
-            (64, 6144, 4096, 1, 32, 3),      # 192 32-row workgroups
-            (64, 12288, 4096, 1, 32, 3),     # 384
+            (64, 12288, 4096, 1, 32, 3),     # 384 (quarter-rows would need 384)
             (48, 24576, 4096, 1, 64, 2),     # 768
-            (64, 2304, 12288, 1, 16, 3),     # 144 16-row workgroups
-            (32, 24576, 4096, 1, 32, 4),     # up to 32 rows: 32-row tiles
-            (48, 100, 512, 1, 16, 3)]:
+            (32, 24576, 4096, 1, 32, 4)]:    # up to 32 rows: 32-row tiles
         t = lib.pick_tactic(M, N, K, S)
         assert (t.stage, t.rows, t.unroll, t.stages) == (quarter, rows, 2, ring), (M, N, K, S, t)
     # not whole 64-K steps per wavefront, four rows or fewer with split-K,
@@ -162,6 +159,37 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
     for M, N, K, S in [(16, 6144, 4160, 1), (4, 6144, 4096, 2), (64, 6144, 4096, 2),
                        (32, 6144, 4096, 4)]:
         assert lib.pick_tactic(M, N, K, S).stage != quarter, (M, N, K, S)
+
+
+def test_pick_quarter_rows_for_33_to_64_rows_without_split(lib):
+    """33..64 rows, split_k 1: two workgroups per tile (one per 32-row block)
+    and the narrowest tile width whose blocks fit the 256 CUs once; wider
+    shapes keep the quarter tiles.  Never with split-K or for the push
+    epilogue's tile choice, which is the quarter or panel rule."""
+    qrows = binding.LOWM_STAGE_QUARTER_ROWS
+    for M, N, K, rows, ring in [
+            (64, 2048, 4096, 16, 4),        # 128 tiles x 2 blocks
+            (64, 4096, 4096, 32, 3),        # 128 x 2
+            (64, 6144, 4096, 48, 3),        # 128 x 2
+            (64, 8192, 4096, 64, 3),        # 128 x 2
+            (33, 6144, 4096, 48, 3),        # a second block of one row
+            (48, 3072, 4096, 32, 3),        # 96 x 2
+            (64, 2304, 12288, 32, 3),       # 72 x 2
+            (48, 100, 512, 16, 4)]:
+        t = lib.pick_tactic(M, N, K, 1)
+        assert (t.stage, t.rows, t.unroll, t.stages) == (qrows, rows, 2, ring), (M, N, K, t)
+        assert lib.check_launch(M, N, K, 1, tactic=t) == binding.LOWM_OK
+        assert lib.check_launch(M, N, K, 1, f32out=True, tactic=t) == binding.LOWM_OK
+    for M, N, K, S in [(64, 12288, 4096, 1), (64, 6144, 4096, 2), (32, 6144, 4096, 1),
+                       (16, 2048, 4096, 1), (64, 6144, 1088, 1)]:
+        assert lib.pick_tactic(M, N, K, S).stage != qrows, (M, N, K, S)
+    # the family exists only without split-K
+    t = binding.tactic("qrows", 48, 2, 3)
+    assert lib.check_launch(64, 6144, 4096, 2, tactic=t) == binding.LOWM_ERR_UNSUPPORTED
+    # blocks of 16..64 rows, none wider than the build's quarter tiles
+    assert lib.check_launch(64, 6144, 4096, 1, tactic=binding.tactic("qrows", 48, 1, 3)) == 0
+    assert lib.check_launch(64, 6144, 4096, 1, tactic=binding.tactic("qrows", 48, 5, 3)) == \
+        binding.LOWM_ERR_UNSUPPORTED
 
 
 def call(lib, A=FAKE_A, W=FAKE_W, C=FAKE_C, M=4, N=64, K=256, S=2, ws=FAKE_WS, f32=False,
@@ -395,6 +423,12 @@ def test_push_validation(lib):
     # the GEMM's own checks still apply
     assert push_call(lib, M=65) == E.LOWM_ERR_UNSUPPORTED
     assert push_call(lib, ws=0) == E.LOWM_ERR_WORKSPACE
+    # no quarter-rows tiles with the push epilogue (each row block would
+    # raise the tile's flags)
+    q = binding.tactic("qrows", 16, 2, 4)
+    assert lib.lib.lowm_gemm_splitk_push(FAKE_A, FAKE_W, C_ADDR, 64, 64, 256, 1, 0, PUSH_ADDR, 64,
+                                         FLAG_ADDR, 1, None, ctypes.byref(q)) == \
+        E.LOWM_ERR_UNSUPPORTED
     assert lib.lib.lowm_last_hip_error() == 0
 
 

@@ -27,6 +27,7 @@ CASES = [
     (16, 1000, 2048, 2),    # quarter tiles, strip epilogue, ragged N
     (64, 520, 2048, 2),     # panel tiles, ragged N
     (16, 6144, 4096, 1),    # quarter tiles without split-K: no workspace
+    (64, 4096, 4096, 1),    # quarter-rows tiles: two row blocks per tile
 ]
 
 

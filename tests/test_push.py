@@ -35,10 +35,13 @@ CASES = [  # M, N, K, split_k
 TACTICS = [None, ("reg", 16, 4, 2), ("lds", 16, 4, 2), ("reg", 32, 4, 2)]
 # panel tiles exist for 17..64 activation rows only
 PANEL_CASES = [(20, 520, 2048, 2), (64, 1000, 4096, 4), (33, 6144, 4096, 1)]
+# 33..64 rows without split-K: the push epilogue's own tile choice (never the
+# quarter-rows tiles, whose row blocks would each raise a tile's flags)
 PAIRS = ([(c, t) for c in CASES for t in TACTICS] +
          [(c, ("panel", 64, 2, 4)) for c in PANEL_CASES] +
          [(c, ("quarter", 32, 2, 3)) for c in CASES] +
-         [((64, 1000, 4096, 4), ("quarter", 64, 2, 2))])
+         [((64, 1000, 4096, 4), ("quarter", 64, 2, 2))] +
+         [((64, 2000, 4096, 1), None), ((40, 3000, 2048, 1), None)])
 
 
 def window(M, N, dev, off=24, extra=40):
