@@ -361,8 +361,11 @@ def trace_breakdown(dev, wl, tactic, launches=4):
     stress = sbg.load("stress")
     M, N, K, S = wl.M, wl.N, wl.K, wl.split_k
     tac = tactic if tactic is not None else stress.pick_tactic(M, N, K, S)
+    from split_bf16_gemm_amd import binding
     tiles = -(-N // tac.rows)
-    grid = (tiles + 7) // 8 * 8 * S
+    # quarter-rows tiles: one workgroup per block of 16*unroll activation rows
+    blocks = -(-M // (16 * tac.unroll)) if tac.stage == binding.LOWM_STAGE_QUARTER_ROWS else 1
+    grid = (tiles + 7) // 8 * 8 * S * blocks
     T = stress.TRACE_SLOTS
     per_set = 2 * K * N + 2 * M * K + 2 * M * N + stress.workspace_bytes(M, N, K, S)
     sets = max(2, math.ceil(2 * MALL_BYTES / per_set) + 1)
@@ -373,7 +376,8 @@ def trace_breakdown(dev, wl, tactic, launches=4):
     torch.cuda.synchronize()
     buf = torch.zeros(grid * T, dtype=torch.int64, device=dev)
     print(f"{wl.name}, tactic {tactic_text(tac)}, {grid} workgroups ({tiles} tiles x "
-          f"split_k {S}); microseconds from the first workgroup's entry")
+          f"split_k {S}" + (f" x {blocks} row blocks" if blocks > 1 else "") +
+          "); microseconds from the first workgroup's entry")
     print("| launch | span | WGs | dispatch | first data | stream | reduction | tail | "
           "last 5 %: dispatch | first data | stream | reduction | tail | end | early owners |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")

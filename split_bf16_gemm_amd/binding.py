@@ -136,7 +136,7 @@ class Library:
         if self.has_stress:
             lib.lowm_stress_configure.argtypes = [ctypes.c_uint, _i, _i, _i, _i, _i, ctypes.c_uint]
             lib.lowm_stress_configure.restype = _i
-            lib.lowm_stress_trace.argtypes = [_vp]
+            lib.lowm_stress_trace.argtypes = [_vp, ctypes.c_size_t]
             lib.lowm_stress_trace.restype = _i
         self.lib = lib
 
@@ -347,10 +347,16 @@ class Library:
 
     def trace(self, buf: Optional[torch.Tensor]):
         """Stress build: per-workgroup timestamps into ``buf`` (int64 device
-        tensor, TRACE_SLOTS per workgroup), or stop tracing with None."""
+        tensor, TRACE_SLOTS per workgroup), or stop tracing with None.  A
+        launch with more workgroups than ``buf`` holds is refused."""
         if not self.has_stress:
             raise RuntimeError(f"{self.path.name} is not a stress build")
-        self.check(self.lib.lowm_stress_trace(None if buf is None else buf.data_ptr()))
+        if buf is None:
+            self.check(self.lib.lowm_stress_trace(None, 0))
+            return
+        if buf.dtype != torch.int64 or not buf.is_cuda or not buf.is_contiguous():
+            raise ValueError("the trace buffer must be a contiguous int64 GPU tensor")
+        self.check(self.lib.lowm_stress_trace(buf.data_ptr(), buf.numel() // self.TRACE_SLOTS))
 
     def configure_stress(self, sites: int = 0, rank: int = -1, wave: int = -1,
                          tile_mod: int = 0, tile_sel: int = 0, step: int = -1,

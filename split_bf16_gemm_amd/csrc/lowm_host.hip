@@ -30,6 +30,8 @@ const Table& table() {
 
 thread_local int g_last_hip_error = 0;
 StressArgs g_stress = {0u, -1, -1, 0, 0, -1, 0u, nullptr};
+// Workgroups the trace buffer has room for (stress build; 0 without one).
+size_t g_trace_capacity = 0;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -466,6 +468,8 @@ int launch_batch(const lowm_gemm_desc* gemms, int count, bool f32out, int M, int
     sl.bid_end = (int)grid;
   }
   for (int g = count; g < kMaxBatch; ++g) bt.g[g] = bt.g[count - 1];
+  // a traced launch (stress build) must fit the trace buffer it writes
+  if (g_stress.trace && grid > g_trace_capacity) return LOWM_ERR_INVALID_ARG;
 
   Args a{};
   a.A = bt.g[0].A;
@@ -780,10 +784,13 @@ int lowm_stress_configure(unsigned site_mask, int rank, int wave, int tile_mod, 
 
 // Stress build only: record per-workgroup timestamps and ids into `buf`
 // (device memory, 10 uint64 per workgroup of the grid: entry, first stage,
-// loop end, reduced, arrived, end, CU id, XCD id, tile, rank; NULL stops
-// tracing).
-int lowm_stress_trace(void* buf) {
+// loop end, reduced, arrived, end, CU id, XCD id, tile, rank), which holds
+// `workgroups` such records; a launch whose grid is larger returns
+// LOWM_ERR_INVALID_ARG before any HIP call.  NULL stops tracing.
+int lowm_stress_trace(void* buf, size_t workgroups) {
+  if (buf && workgroups == 0) return LOWM_ERR_INVALID_ARG;
   lowm::g_stress.trace = static_cast<uint64_t*>(buf);
+  lowm::g_trace_capacity = buf ? workgroups : 0;
   return LOWM_OK;
 }
 #endif

@@ -489,3 +489,20 @@ def test_quarter_tiles_built_where_lds_allows(lib):
                 assert (rc == binding.LOWM_OK) == want, (M, rows, ring, rc)
     t = binding.tactic("quarter", 32, 2, 2)
     assert lib.check_launch(32, 6144, 4096 + 128, 1, tactic=t) == binding.LOWM_ERR_UNSUPPORTED
+
+
+def test_trace_buffer_bounds_the_grid(stress_lib):
+    """Stress build: a launch whose grid has more workgroups than the trace
+    buffer holds is refused before any HIP call (a buffer of one record
+    against a grid of 16 here), and a buffer without room is rejected."""
+    lib = stress_lib
+    E = binding
+    assert lib.lib.lowm_stress_trace(FAKE, 0) == E.LOWM_ERR_INVALID_ARG
+    assert lib.lib.lowm_stress_trace(FAKE, 1) == E.LOWM_OK
+    try:
+        assert call(lib) == E.LOWM_ERR_INVALID_ARG          # 4 tiles -> 8, x split_k 2
+        assert call(lib, M=64, N=64, S=1, tac=binding.tactic("qrows", 16, 2, 4)) == \
+            E.LOWM_ERR_INVALID_ARG                          # 8 workgroups x 2 row blocks
+    finally:
+        assert lib.lib.lowm_stress_trace(None, 0) == E.LOWM_OK
+    assert lib.lib.lowm_last_hip_error() == 0
