@@ -72,7 +72,7 @@ size_t act_lds_bytes(int M, int nvec) { return (size_t)M * (nvec + 1) * 16; }
 KernelFn select_kernel(bool f32out, int M, int S, int nvec, const lowm_tactic& t,
                        size_t* dyn_lds, bool push = false);
 
-// Default tactic, in order: quarter-rows tiles for 33..64 rows without
+// Default tactic, in order: quarter-rows tiles for 49..64 rows without
 // split-K where their grid fits the device once, quarter tiles where the
 // rules below name them, panel tiles above 16 rows, line-pair tiles, the
 // register ring.
@@ -136,11 +136,13 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   //     32-row workgroups W: <= 96 rows 16 ring 3, <= 192 rows 32 ring 3,
   //     <= 384 rows 16 ring 2, else rows 32 ring 2 (M 16 N 6144 split_k 2 /
   //     4 / 8: 12.3 / 12.5 / 15.5 us against 14.4 / 15.1 / 17.2);
-  //   - split_k 1, M > 32: rows 16 ring 3 where that gives no more than 192
-  //     workgroups, else rows 32 ring 3 up to 384 workgroups, else rows 64
-  //     ring 2 (M 64 N 6144: 17.1 against 17.6 for the panel tiles; N 24576:
-  //     51.7 against 56.6 for 32-row and 48.7 for 64-row panel tiles, taken
-  //     so that the summation order does not depend on N);
+  //   - split_k 1, M > 32 (where the quarter-rows tiles above do not
+  //     apply): rows 16 ring 3 where that gives no more than 192
+  //     workgroups, else rows 32 ring 3 up to 256 workgroups, else rows 64
+  //     ring 2 (M 64 N 8192: 18.1 against 24.6 for rows 64; N 12288: 26.5
+  //     against 31.9 for rows 32, whose 384 workgroups take two rounds;
+  //     N 24576: 50.5 against 46.8 for 64-row panel tiles, taken so that the
+  //     summation order does not depend on N);
   //   - split_k 2, 16 < M <= 32: rows 16 ring 3 where that gives no more than
   //     192 workgroups, else rows 64 ring 3 (M 32 N 6144: 14.8 against 15.1;
   //     N 24576: 47.4 against 45.1, again one order for every N).
@@ -157,18 +159,21 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
       t->rows = rows;
       return provides({kStageQuarter, 2, ring});
     };
-    // Quarter-rows tiles for 33..64 rows without split-K (not for the push
+    // Quarter-rows tiles for 49..64 rows without split-K (not for the push
     // epilogue): two workgroups per tile, one per 32-row block, and the
-    // narrowest tile width (16..64 columns) at which the blocks fill the 256
-    // CUs once; above that width the rules below.  Measured on MI355X at
-    // M 64, K 4096 against the quarter default: N 2048 / 4096 / 6144 / 8192
-    // 9.3 / 12.2 / 15.4 / 18.4 us against 13.4 / 16.3 / 17.1 / 20.2 (the
-    // activation bytes per CU fall from 512 KB to 256 KB); M 40 / 48 / 56 at
-    // N 6144 and M 64 at K 8192 and 16384 gain as well.  Same summation
-    // order, so the same bits, as the quarter tiles.
-    if (M > 32 && S == 1 && !push) {
+    // narrowest tile width (16..48 columns) at which the blocks fill the 256
+    // CUs once; otherwise the rules below.  Measured on MI355X (bench.py
+    // --tactic-matrix) at M 64, K 4096 against the quarter tiles: N 2048 /
+    // 4096 / 6144 9.3 / 12.2 / 15.4 us against 13.3 / 14.2 / 17.0; N 6144
+    // K 8192 29.8 against 31.6; N 2304 K 12288 31.0 against 35.2.  Each
+    // workgroup moves 32 activation rows and 16..48 weight rows per K step
+    // where the quarter tiles move M and 16..32: at 33..48 rows that is no
+    // fewer bytes (M 40, N 6144: 15.5 against 14.7), and at N 8192 the
+    // 64-column blocks lose to 32-row quarter tiles (18.7 against 18.1).
+    // Same summation order, so the same bits, as the quarter tiles.
+    if (M > 48 && S == 1 && !push) {
       const long blocks = (M + 31) / 32;
-      for (int nb = 1; nb <= 4; ++nb)
+      for (int nb = 1; nb <= 3; ++nb)
         if ((long)((N + 16 * nb - 1) / (16 * nb)) * blocks <= 256) {
           t->rows = 16 * nb;
           t->stage = kStageQuarterRows;
@@ -193,7 +198,7 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
     } else if (M > 16 && S == 1) {
       if (w16 <= 192 ? quarter(16, 3)
                      : M <= 32 ? (quarter(32, 4) || quarter(32, 3))
-                               : w32 <= 384 ? quarter(32, 3) : quarter(64, 2))
+                               : w32 <= 256 ? quarter(32, 3) : quarter(64, 2))
         return LOWM_OK;
     } else if (M > 16 && M <= 32 && S == 2) {
       if (w16 <= 192 ? quarter(16, 3) : quarter(64, 3)) return LOWM_OK;

@@ -148,9 +148,13 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (24, 6144, 4096, 2, 64, 3),
             (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
             (20, 3072, 4096, 1, 16, 3),
-            (64, 12288, 4096, 1, 32, 3),     # 384 (quarter-rows would need 384)
+            (64, 8192, 4096, 1, 32, 3),      # 256 32-row workgroups
+            (64, 12288, 4096, 1, 64, 2),     # 384: 64-row tiles
+            (40, 6144, 4096, 1, 32, 3),      # 33..48 rows: no quarter-rows tiles
+            (48, 3072, 4096, 1, 16, 3),      # 192 16-row workgroups
             (48, 24576, 4096, 1, 64, 2),     # 768
-            (32, 24576, 4096, 1, 32, 4)]:    # up to 32 rows: 32-row tiles
+            (32, 24576, 4096, 1, 32, 4),     # up to 32 rows: 32-row tiles
+            (48, 100, 512, 1, 16, 3)]:
         t = lib.pick_tactic(M, N, K, S)
         assert (t.stage, t.rows, t.unroll, t.stages) == (quarter, rows, 2, ring), (M, N, K, S, t)
     # not whole 64-K steps per wavefront, four rows or fewer with split-K,
@@ -162,26 +166,26 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
 
 
 def test_pick_quarter_rows_for_33_to_64_rows_without_split(lib):
-    """33..64 rows, split_k 1: two workgroups per tile (one per 32-row block)
-    and the narrowest tile width whose blocks fit the 256 CUs once; wider
-    shapes keep the quarter tiles.  Never with split-K or for the push
-    epilogue's tile choice, which is the quarter or panel rule."""
+    """49..64 rows, split_k 1: two workgroups per tile (one per 32-row block)
+    and the narrowest tile width (up to 48 columns) whose blocks fit the 256
+    CUs once; wider shapes and 33..48 rows keep the quarter tiles.  Never
+    with split-K or for the push epilogue's tile choice."""
     qrows = binding.LOWM_STAGE_QUARTER_ROWS
     for M, N, K, rows, ring in [
             (64, 2048, 4096, 16, 4),        # 128 tiles x 2 blocks
             (64, 4096, 4096, 32, 3),        # 128 x 2
             (64, 6144, 4096, 48, 3),        # 128 x 2
-            (64, 8192, 4096, 64, 3),        # 128 x 2
-            (33, 6144, 4096, 48, 3),        # a second block of one row
-            (48, 3072, 4096, 32, 3),        # 96 x 2
+            (49, 6144, 4096, 48, 3),        # a second block of 17 rows
+            (56, 3072, 4096, 32, 3),        # 96 x 2
             (64, 2304, 12288, 32, 3),       # 72 x 2
-            (48, 100, 512, 16, 4)]:
+            (64, 100, 512, 16, 4)]:
         t = lib.pick_tactic(M, N, K, 1)
         assert (t.stage, t.rows, t.unroll, t.stages) == (qrows, rows, 2, ring), (M, N, K, t)
         assert lib.check_launch(M, N, K, 1, tactic=t) == binding.LOWM_OK
         assert lib.check_launch(M, N, K, 1, f32out=True, tactic=t) == binding.LOWM_OK
-    for M, N, K, S in [(64, 12288, 4096, 1), (64, 6144, 4096, 2), (32, 6144, 4096, 1),
-                       (16, 2048, 4096, 1), (64, 6144, 1088, 1)]:
+    for M, N, K, S in [(64, 12288, 4096, 1), (64, 8192, 4096, 1), (64, 6144, 4096, 2),
+                       (48, 2048, 4096, 1), (32, 6144, 4096, 1), (16, 2048, 4096, 1),
+                       (64, 6144, 1088, 1)]:
         assert lib.pick_tactic(M, N, K, S).stage != qrows, (M, N, K, S)
     # the family exists only without split-K
     t = binding.tactic("qrows", 48, 2, 3)

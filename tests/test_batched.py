@@ -27,7 +27,7 @@ CASES = [
     (24, [6144, 512], 4096, 2),            # quarter tiles: 16 rows for the batch, 64 alone
     (64, [6144, 1024], 4096, 1),           # quarter tiles: 16 rows for the batch, 32 alone
     (64, [2048, 6144], 4096, 1),           # quarter-rows tiles: 16 columns for the batch, 48 alone
-    (40, [12288, 1000], 2048, 1),          # quarter-rows for the batch, quarter tiles alone
+    (56, [12288, 1000], 2048, 1),          # quarter-rows for the batch, 64-row quarter tiles alone
 ]
 
 
