@@ -272,12 +272,12 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
      {1, 4, 2, 4},
      {1, 1, 2, 1}},
     // 32 < M <= 64
-    {{1, 1, 8, 8},
-     {1, 1, 8, 8},
+    {{1, 1, 1, 8},
+     {1, 1, 1, 8},
      {1, 1, 4, 4},
-     {1, 1, 2, 2},
-     {1, 1, 2, 2},
-     {1, 1, 1, 2}}};
+     {1, 1, 1, 2},
+     {1, 1, 1, 1},
+     {1, 1, 2, 2}}};
 
 int nearest_log2_index(double x, double base, int last) {
   const int i = (int)floor(log2(x / base) + 0.5);
