@@ -48,11 +48,12 @@ PLANS = [
 
 # (workload, tactic): the default tactic at the headline shape is the line-pair
 # tiles; the panel tiles run at M 64, split_k 2, the quarter tiles at M 16,
-# split_k 2 (each the default there).
+# split_k 2, the quarter-rows tiles at M 64, split_k 1 (each the default there).
 CASES = [(workloads.HEADLINE, None), (workloads.HEADLINE, binding.tactic("lds", 16, 4, 2)),
          (workloads.HEADLINE, binding.tactic("reg", 16, 8, 2)),
          (workloads.by_name("sweep_m64_n6144_k4096_s2"), None),
-         (workloads.by_name("sweep_m16_n6144_k4096_s2"), None)]
+         (workloads.by_name("sweep_m16_n6144_k4096_s2"), None),
+         (workloads.by_name("sweep_m64_n6144_k4096_s1"), None)]
 
 
 @pytest.fixture(scope="module")
@@ -71,7 +72,7 @@ def launch(lib, ops, wl, tactic):
 
 
 @pytest.mark.parametrize("case", CASES, ids=["line_default", "lds_ns2", "reg_u8_ns2", "panel_m64",
-                                          "quarter_m16"])
+                                          "quarter_m16", "qrows_m64"])
 @pytest.mark.parametrize("plan", PLANS, ids=[p[0] for p in PLANS])
 def test_under_stalls(libs, plan, case):
     base, stress = libs
@@ -92,7 +93,8 @@ def test_under_stalls(libs, plan, case):
         finally:
             stress.configure_stress(0)
         assert np.array_equal(got, ref), f"{name}, {d} ns: output differs from the unstalled run"
-    assert not ws.cpu().numpy().any(), "the workspace (counters, partial slots) was left non-zero"
+    if ws is not None:
+        assert not ws.cpu().numpy().any(), "the workspace (counters, partial slots) was left non-zero"
 
 
 @pytest.mark.parametrize("wl", workloads.sweep(), ids=lambda w: w.name)
