@@ -189,6 +189,17 @@ def test_quarter_rows_tiles(lib, M, N, K):
     assert ran >= 8, ran
 
 
+@pytest.mark.parametrize("M,N,K", [(49, 6144, 4096), (57, 3000, 2048), (63, 100, 1024),
+                                   (50, 4096, 8192)])
+def test_quarter_rows_by_default(lib, M, N, K):
+    """49..63 rows without split-K: the default tactic is the quarter-rows
+    tiles with a short second row block; judged against the oracle."""
+    t = lib.pick_tactic(M, N, K, 1)
+    assert t.stage == sbg.binding.LOWM_STAGE_QUARTER_ROWS, t
+    wl = workloads.Workload(f"qrows_default_{M}_{N}_{K}", M, N, K, 1, seed_a=M + 700, seed_w=N + 800)
+    check_random(lib, wl)
+
+
 def test_every_tactic_random(lib):
     """M 20 (two row blocks) with whole 256-K slices: every tactic family
     applies (5 register/LDS variants at 16 rows, 4 at 32, 3 line-pair rings,
