@@ -134,8 +134,10 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   //     10.01 / 12.83 us against 9.86 / 10.00 / 10.18 / 12.96 with ring 3;
   //   - split_k >= 2, 4 < M <= 16: the tile width and ring by the number of
   //     32-row workgroups W: <= 96 rows 16 ring 3, <= 192 rows 32 ring 3,
+  //     then rows 48 ring 3 where those number <= 256 (one per CU), then
   //     <= 384 rows 16 ring 2, else rows 32 ring 2 (M 16 N 6144 split_k 2 /
-  //     4 / 8: 12.3 / 12.5 / 15.5 us against 14.4 / 15.1 / 17.2);
+  //     4 / 8: 11.6 / 12.3 / 15.5 us; split_k 2 with rows 16 ring 2 12.6,
+  //     M 8 11.4 against 11.6);
   //   - split_k 1, M > 32 (where the quarter-rows tiles above do not
   //     apply): rows 16 ring 3 where that gives no more than 192
   //     workgroups, else rows 32 ring 3 up to 256 workgroups, else rows 64
@@ -144,8 +146,9 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   //     N 24576: 50.5 against 46.8 for 64-row panel tiles, taken so that the
   //     summation order does not depend on N);
   //   - split_k 2, 16 < M <= 32: rows 16 ring 3 where that gives no more than
-  //     192 workgroups, else rows 64 ring 3 (M 32 N 6144: 14.8 against 15.1;
-  //     N 24576: 47.4 against 45.1, again one order for every N).
+  //     192 workgroups, else rows 48 ring 3 where those number <= 256, else
+  //     rows 64 ring 3 (M 32 N 6144: 13.4 against 14.2 for rows 64; N 24576:
+  //     47.4 against 45.1, again one order for every N).
   // The line-pair tiles stay faster for M <= 4 with split_k >= 2 (their last
   // rank folds without the exchange's round trips), the panel tiles for
   // M > 32 with split-K and for split_k >= 4 above 16 rows.  Every choice
@@ -155,6 +158,7 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   if (nvec % 32 == 0) {
     const long w16 = (long)((N + 15) / 16) * S;
     const long w32 = (long)((N + 31) / 32) * S;
+    const long w48 = (long)((N + 47) / 48) * S;
     auto quarter = [&](int rows, int ring) {
       t->rows = rows;
       return provides({kStageQuarter, 2, ring});
@@ -193,7 +197,9 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
       if ((w32 <= 256 && quarter(32, 4)) || quarter(32, 3)) return LOWM_OK;
     } else if (M > 4 && M <= 16) {
       if (w32 <= 96 ? quarter(16, 3)
-                    : w32 <= 192 ? quarter(32, 3) : w32 <= 384 ? quarter(16, 2) : quarter(32, 2))
+                    : w32 <= 192 ? quarter(32, 3)
+                                 : w48 <= 256 ? quarter(48, 3)
+                                              : w32 <= 384 ? quarter(16, 2) : quarter(32, 2))
         return LOWM_OK;
     } else if (M > 16 && S == 1) {
       if (w16 <= 192 ? quarter(16, 3)
@@ -201,7 +207,8 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
                                : w32 <= 256 ? quarter(32, 3) : quarter(64, 2))
         return LOWM_OK;
     } else if (M > 16 && M <= 32 && S == 2) {
-      if (w16 <= 192 ? quarter(16, 3) : quarter(64, 3)) return LOWM_OK;
+      if (w16 <= 192 ? quarter(16, 3) : w48 <= 256 ? quarter(48, 3) : quarter(64, 3))
+        return LOWM_OK;
     }
   }
   // More than 16 activation rows: panel tiles (the activation operand of a
@@ -251,17 +258,17 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
      {1, 2, 2, 8},    // N 12288
      {1, 1, 2, 8}},   // N 24576
     // 4 < M <= 8
-    {{2, 4, 8, 8},
-     {2, 4, 4, 4},
-     {2, 2, 2, 4},
+    {{4, 8, 8, 8},
+     {1, 4, 4, 4},
+     {1, 2, 2, 4},
      {1, 1, 2, 4},
      {1, 1, 2, 4},
      {1, 1, 2, 4}},
     // 8 < M <= 16
-    {{4, 4, 8, 8},
+    {{4, 4, 4, 8},
+     {1, 2, 4, 8},
      {2, 4, 4, 4},
-     {2, 2, 2, 4},
-     {1, 1, 4, 4},
+     {1, 1, 2, 4},
      {1, 2, 2, 4},
      {1, 1, 2, 4}},
     // 16 < M <= 32
@@ -269,7 +276,7 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
      {1, 2, 2, 8},
      {1, 1, 4, 4},
      {1, 1, 2, 2},
-     {1, 4, 2, 4},
+     {1, 1, 2, 4},
      {1, 1, 2, 1}},
     // 32 < M <= 64
     {{1, 1, 1, 8},

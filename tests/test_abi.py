@@ -139,13 +139,15 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (16, 6144, 4096, 1, 32, 4), (8, 6144, 4096, 1, 32, 4), (1, 6144, 4096, 1, 32, 4),
             (4, 8192, 4096, 1, 32, 4),       # 256 32-row workgroups: ring 4
             (4, 24576, 4096, 1, 32, 3),      # 768: ring 3 fits two per CU
-            (8, 6144, 4096, 2, 16, 2),       # 384 32-row workgroups
+            (8, 6144, 4096, 2, 48, 3),       # 384 32-row, 256 48-row workgroups
+            (8, 12288, 4096, 2, 32, 2),      # 768 32-row, 512 48-row workgroups
             (16, 6144, 4096, 4, 32, 2),      # 768
             (16, 1536, 8192, 2, 16, 3),      # 96
             (8, 1536, 8192, 4, 32, 3),       # 192
             (12, 6144, 4096, 8, 32, 2),      # 1536
             (32, 6144, 4096, 1, 32, 4),      # 384 16-row workgroups
-            (24, 6144, 4096, 2, 64, 3),
+            (24, 6144, 4096, 2, 48, 3),      # 256 48-row workgroups
+            (24, 12288, 4096, 2, 64, 3),     # 512 48-row workgroups
             (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
             (20, 3072, 4096, 1, 16, 3),
             (64, 8192, 4096, 1, 32, 3),      # 256 32-row workgroups
@@ -323,7 +325,7 @@ def test_pick_split_k(lib):
     assert lib.pick_split_k(64, 6144, 4096) == 1
     assert lib.pick_split_k(64, 3072, 8192) == 4
     # rows: M <= 4, <= 8, <= 16, <= 32, else the M 64 measurements
-    assert lib.pick_split_k(4, 768, 2048) == 4 and lib.pick_split_k(5, 768, 2048) == 2
+    assert lib.pick_split_k(4, 768, 4096) == 4 and lib.pick_split_k(5, 768, 4096) == 8
     assert lib.pick_split_k(9, 1536, 8192) == 4 and lib.pick_split_k(8, 768, 8192) == 8
     assert lib.pick_split_k(17, 768, 8192) == 2 and lib.pick_split_k(33, 1536, 2048) == 1
     assert lib.pick_split_k(64, 768, 16384) == 8 and lib.pick_split_k(64, 768, 8192) == 1
