@@ -139,12 +139,14 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   //     4 / 8: 11.6 / 12.3 / 15.5 us; split_k 2 with rows 16 ring 2 12.6,
   //     M 8 11.4 against 11.6);
   //   - split_k 1, M > 32 (where the quarter-rows tiles above do not
-  //     apply): rows 16 ring 3 where that gives no more than 192
-  //     workgroups, else rows 32 ring 3 up to 256 workgroups, else rows 64
-  //     ring 2 (M 64 N 8192: 18.1 against 24.6 for rows 64; N 12288: 26.5
-  //     against 31.9 for rows 32, whose 384 workgroups take two rounds;
-  //     N 24576: 50.5 against 46.8 for 64-row panel tiles, taken so that the
-  //     summation order does not depend on N);
+  //     apply): the tile width of 16..64 rows with the fewest rounds of 256
+  //     workgroups times rows loaded per K step (activation blocks plus
+  //     weight rows); ring 3 where it fits, else 2.  Every measured winner
+  //     is that choice: M 64 N 8192 / 12288 / 16384 / 24576 rows 32 / 48 /
+  //     64 / 48 (18.1 / 23.7 / 29.2 / 45.5 us, the others 18.1-24.5 /
+  //     26.2-31.5 / 35.1-40.6 / 50.6-52.3), M 40 N 6144 rows 32 (14.7),
+  //     M 40 N 24576 and M 48 N 12288 rows 48 (37.6, 20.8 against 45.0-46.0
+  //     and 23.6-28.9);
   //   - split_k 2, 16 < M <= 32: rows 16 ring 3 where that gives no more than
   //     192 workgroups, else rows 48 ring 3 where those number <= 256, else
   //     rows 64 ring 3 (M 32 N 6144: 13.4 against 14.2 for rows 64; N 24576:
@@ -201,11 +203,25 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
                                  : w48 <= 256 ? quarter(48, 3)
                                               : w32 <= 384 ? quarter(16, 2) : quarter(32, 2))
         return LOWM_OK;
-    } else if (M > 16 && S == 1) {
-      if (w16 <= 192 ? quarter(16, 3)
-                     : M <= 32 ? (quarter(32, 4) || quarter(32, 3))
-                               : w32 <= 256 ? quarter(32, 3) : quarter(64, 2))
-        return LOWM_OK;
+    } else if (M > 16 && M <= 32 && S == 1) {
+      if (w16 <= 192 ? quarter(16, 3) : (quarter(32, 4) || quarter(32, 3))) return LOWM_OK;
+    } else if (M > 32 && S == 1) {
+      // The tile width whose workgroups move the fewest bytes in all: rounds
+      // of up to 256 workgroups (one per CU) times the rows each loads per K
+      // step (its 16-row blocks of activations plus its weight rows).
+      const long act_rows = 16L * ((M + 15) / 16);
+      int best = 1;
+      long best_cost = 0;
+      for (int nb = 1; nb <= 4; ++nb) {
+        const long wgs = (long)((N + 16 * nb - 1) / (16 * nb));
+        const long cost = (wgs + 255) / 256 * (act_rows + 16 * nb);
+        if (nb == 1 || cost < best_cost) {
+          best = nb;
+          best_cost = cost;
+        }
+      }
+      const int ring = best <= 2 || (best == 3 && M <= 48) ? 3 : 2;
+      if (quarter(16 * best, ring) || quarter(16 * best, 2)) return LOWM_OK;
     } else if (M > 16 && M <= 32 && S == 2) {
       if (w16 <= 192 ? quarter(16, 3) : w48 <= 256 ? quarter(48, 3) : quarter(64, 3))
         return LOWM_OK;

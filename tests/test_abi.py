@@ -151,10 +151,13 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
             (20, 3072, 4096, 1, 16, 3),
             (64, 8192, 4096, 1, 32, 3),      # 256 32-row workgroups
-            (64, 12288, 4096, 1, 64, 2),     # 384: 64-row tiles
+            (64, 12288, 4096, 1, 48, 2),     # 256 48-row workgroups: one round
+            (64, 16384, 4096, 1, 64, 2),     # 256 64-row workgroups
+            (64, 24576, 4096, 1, 48, 2),     # two rounds of 48-row tiles
             (40, 6144, 4096, 1, 32, 3),      # 33..48 rows: no quarter-rows tiles
             (48, 3072, 4096, 1, 16, 3),      # 192 16-row workgroups
-            (48, 24576, 4096, 1, 64, 2),     # 768
+            (48, 24576, 4096, 1, 48, 3),     # two rounds of 48-row tiles
+            (40, 12288, 4096, 1, 48, 3),
             (32, 24576, 4096, 1, 32, 4),     # up to 32 rows: 32-row tiles
             (48, 100, 512, 1, 16, 3)]:
         t = lib.pick_tactic(M, N, K, S)
