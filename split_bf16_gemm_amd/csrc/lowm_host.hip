@@ -300,7 +300,7 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
      {1, 1, 4, 4},
      {1, 1, 1, 2},
      {1, 1, 1, 1},
-     {1, 1, 2, 2}}};
+     {1, 1, 1, 2}}};
 
 int nearest_log2_index(double x, double base, int last) {
   const int i = (int)floor(log2(x / base) + 0.5);
