@@ -332,7 +332,8 @@ def test_pick_split_k(lib):
     assert lib.pick_split_k(9, 1536, 8192) == 4 and lib.pick_split_k(8, 768, 8192) == 8
     assert lib.pick_split_k(17, 768, 8192) == 2 and lib.pick_split_k(33, 1536, 2048) == 1
     assert lib.pick_split_k(64, 768, 16384) == 8 and lib.pick_split_k(64, 768, 8192) == 1
-    assert lib.pick_split_k(64, 24576, 8192) == 2 and lib.pick_split_k(64, 12288, 16384) == 1
+    assert lib.pick_split_k(64, 24576, 16384) == 2 and lib.pick_split_k(64, 12288, 16384) == 1
+    assert lib.pick_split_k(64, 24576, 8192) == 1
     # always a split_k the launch accepts
     for M in (1, 4, 9, 16, 33, 64):
         for N in (1, 100, 768, 2304, 6144, 100000):
