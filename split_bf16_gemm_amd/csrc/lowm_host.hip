@@ -134,10 +134,11 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   //     10.01 / 12.83 us against 9.86 / 10.00 / 10.18 / 12.96 with ring 3;
   //   - split_k >= 2, 4 < M <= 16: the tile width and ring by the number of
   //     32-row workgroups W: <= 96 rows 16 ring 3, <= 192 rows 32 ring 3,
-  //     then rows 48 ring 3 where those number <= 256 (one per CU), then
-  //     <= 384 rows 16 ring 2, else rows 32 ring 2 (M 16 N 6144 split_k 2 /
-  //     4 / 8: 11.6 / 12.3 / 15.5 us; split_k 2 with rows 16 ring 2 12.6,
-  //     M 8 11.4 against 11.6);
+  //     then rows 48 ring 3 where those number <= 256 (one per CU), else
+  //     rows 48 ring 2 (M 16 N 6144 split_k 2 / 4 / 8: 11.6 / 12.3 / 15.5
+  //     us; split_k 2 with rows 16 ring 2 12.6, M 8 11.4 against 11.6; in
+  //     two or more rounds rows 48 ring 2 beat rows 32 ring 2 by 1.6-3 %:
+  //     M 16 N 12288 / 24576 split_k 2 19.3 / 36.7 against 19.9 / 37.7);
   //   - split_k 1, M > 32 (where the quarter-rows tiles above do not
   //     apply): the tile width of 16..64 rows with the fewest rounds of 256
   //     workgroups times rows loaded per K step (activation blocks plus
@@ -147,10 +148,11 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   //     26.2-31.5 / 35.1-40.6 / 50.6-52.3), M 40 N 6144 rows 32 (14.7),
   //     M 40 N 24576 and M 48 N 12288 rows 48 (37.6, 20.8 against 45.0-46.0
   //     and 23.6-28.9);
-  //   - split_k 2, 16 < M <= 32: rows 16 ring 3 where that gives no more than
-  //     192 workgroups, else rows 48 ring 3 where those number <= 256, else
-  //     rows 64 ring 3 (M 32 N 6144: 13.4 against 14.2 for rows 64; N 24576:
-  //     47.4 against 45.1, again one order for every N).
+  //   - split_k 2, 16 < M <= 32: the width with the fewest rounds times rows
+  //     loaded (as for 33..64 rows below), ring 3; it picks every measured
+  //     winner: M 32 N 3072 / 6144 / 12288 rows 32 / 48 / 48 (10.1 / 13.2 /
+  //     25.1 us, the best other width 11.5 / 14.2 / 26.8), M 24 N 24576
+  //     rows 64 (44.6, against 45.0 for rows 32).
   // The line-pair tiles stay faster for M <= 4 with split_k >= 2 (their last
   // rank folds without the exchange's round trips), the panel tiles for
   // M > 32 with split-K and for split_k >= 4 above 16 rows.  Every choice
@@ -164,6 +166,24 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
     auto quarter = [&](int rows, int ring) {
       t->rows = rows;
       return provides({kStageQuarter, 2, ring});
+    };
+    // The tile width of 16..64 weight rows whose workgroups move the fewest
+    // bytes in all: rounds of up to 256 workgroups (one per CU) times the rows
+    // each loads per K step (its 16-row blocks of activations plus its weight
+    // rows); returns the width in 16-row groups.
+    auto fewest_rows = [&]() {
+      const long act_rows = 16L * ((M + 15) / 16);
+      int best = 1;
+      long best_cost = 0;
+      for (int nb = 1; nb <= 4; ++nb) {
+        const long wgs = (long)((N + 16 * nb - 1) / (16 * nb)) * S;
+        const long cost = (wgs + 255) / 256 * (act_rows + 16 * nb);
+        if (nb == 1 || cost < best_cost) {
+          best = nb;
+          best_cost = cost;
+        }
+      }
+      return best;
     };
     // Quarter-rows tiles for 49..64 rows without split-K (not for the push
     // epilogue): two workgroups per tile, one per 32-row block, and the
@@ -200,31 +220,16 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
     } else if (M > 4 && M <= 16) {
       if (w32 <= 96 ? quarter(16, 3)
                     : w32 <= 192 ? quarter(32, 3)
-                                 : w48 <= 256 ? quarter(48, 3)
-                                              : w32 <= 384 ? quarter(16, 2) : quarter(32, 2))
+                                 : w48 <= 256 ? quarter(48, 3) : quarter(48, 2))
         return LOWM_OK;
     } else if (M > 16 && M <= 32 && S == 1) {
       if (w16 <= 192 ? quarter(16, 3) : (quarter(32, 4) || quarter(32, 3))) return LOWM_OK;
     } else if (M > 32 && S == 1) {
-      // The tile width whose workgroups move the fewest bytes in all: rounds
-      // of up to 256 workgroups (one per CU) times the rows each loads per K
-      // step (its 16-row blocks of activations plus its weight rows).
-      const long act_rows = 16L * ((M + 15) / 16);
-      int best = 1;
-      long best_cost = 0;
-      for (int nb = 1; nb <= 4; ++nb) {
-        const long wgs = (long)((N + 16 * nb - 1) / (16 * nb));
-        const long cost = (wgs + 255) / 256 * (act_rows + 16 * nb);
-        if (nb == 1 || cost < best_cost) {
-          best = nb;
-          best_cost = cost;
-        }
-      }
+      const int best = fewest_rows();
       const int ring = best <= 2 || (best == 3 && M <= 48) ? 3 : 2;
       if (quarter(16 * best, ring) || quarter(16 * best, 2)) return LOWM_OK;
     } else if (M > 16 && M <= 32 && S == 2) {
-      if (w16 <= 192 ? quarter(16, 3) : w48 <= 256 ? quarter(48, 3) : quarter(64, 3))
-        return LOWM_OK;
+      if (quarter(16 * fewest_rows(), 3)) return LOWM_OK;
     }
   }
   // More than 16 activation rows: panel tiles (the activation operand of a

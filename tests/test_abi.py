@@ -140,14 +140,16 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (4, 8192, 4096, 1, 32, 4),       # 256 32-row workgroups: ring 4
             (4, 24576, 4096, 1, 32, 3),      # 768: ring 3 fits two per CU
             (8, 6144, 4096, 2, 48, 3),       # 384 32-row, 256 48-row workgroups
-            (8, 12288, 4096, 2, 32, 2),      # 768 32-row, 512 48-row workgroups
-            (16, 6144, 4096, 4, 32, 2),      # 768
+            (8, 12288, 4096, 2, 48, 2),      # 512 48-row workgroups: two rounds
+            (16, 6144, 4096, 4, 48, 2),      # 768 32-row, 512 48-row workgroups
             (16, 1536, 8192, 2, 16, 3),      # 96
             (8, 1536, 8192, 4, 32, 3),       # 192
-            (12, 6144, 4096, 8, 32, 2),      # 1536
+            (12, 6144, 4096, 8, 48, 2),      # 1536 32-row workgroups
             (32, 6144, 4096, 1, 32, 4),      # 384 16-row workgroups
             (24, 6144, 4096, 2, 48, 3),      # 256 48-row workgroups
-            (24, 12288, 4096, 2, 64, 3),     # 512 48-row workgroups
+            (24, 12288, 4096, 2, 48, 3),     # fewest rounds x rows: 48 rows, two rounds
+            (24, 24576, 4096, 2, 64, 3),     # 64 rows, three rounds
+            (32, 3072, 4096, 2, 32, 3),      # one round of 32-row workgroups
             (32, 1536, 8192, 2, 16, 3),      # 192 16-row workgroups
             (20, 3072, 4096, 1, 16, 3),
             (64, 8192, 4096, 1, 32, 3),      # 256 32-row workgroups
