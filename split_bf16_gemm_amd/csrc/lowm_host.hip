@@ -279,23 +279,23 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
      {1, 2, 2, 8},    // N 12288
      {1, 1, 2, 8}},   // N 24576
     // 4 < M <= 8
-    {{4, 8, 8, 8},
-     {1, 4, 4, 4},
-     {1, 2, 2, 4},
-     {1, 1, 2, 4},
-     {1, 1, 2, 4},
-     {1, 1, 2, 4}},
-    // 8 < M <= 16
-    {{4, 4, 4, 8},
-     {1, 2, 4, 8},
+    {{4, 4, 8, 8},
+     {2, 4, 4, 4},
      {2, 4, 4, 4},
      {1, 1, 2, 4},
      {1, 2, 2, 4},
      {1, 1, 2, 4}},
+    // 8 < M <= 16
+    {{4, 4, 8, 8},
+     {2, 4, 4, 8},
+     {1, 4, 4, 4},
+     {1, 1, 2, 4},
+     {1, 2, 2, 4},
+     {1, 1, 2, 4}},
     // 16 < M <= 32
-    {{1, 2, 2, 8},
+    {{2, 2, 2, 8},
      {1, 2, 2, 8},
-     {1, 1, 4, 4},
+     {1, 1, 2, 4},
      {1, 1, 2, 2},
      {1, 1, 2, 4},
      {1, 1, 2, 1}},

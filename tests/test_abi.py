@@ -330,7 +330,7 @@ def test_pick_split_k(lib):
     assert lib.pick_split_k(64, 6144, 4096) == 1
     assert lib.pick_split_k(64, 3072, 8192) == 4
     # rows: M <= 4, <= 8, <= 16, <= 32, else the M 64 measurements
-    assert lib.pick_split_k(4, 768, 4096) == 4 and lib.pick_split_k(5, 768, 4096) == 8
+    assert lib.pick_split_k(4, 768, 8192) == 4 and lib.pick_split_k(5, 768, 8192) == 8
     assert lib.pick_split_k(9, 1536, 8192) == 4 and lib.pick_split_k(8, 768, 8192) == 8
     assert lib.pick_split_k(17, 768, 8192) == 2 and lib.pick_split_k(33, 1536, 2048) == 1
     assert lib.pick_split_k(64, 768, 16384) == 8 and lib.pick_split_k(64, 768, 8192) == 1
