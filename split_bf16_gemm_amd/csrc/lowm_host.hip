@@ -135,10 +135,12 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
   //   - split_k >= 2, 4 < M <= 16: the tile width and ring by the number of
   //     32-row workgroups W: <= 96 rows 16 ring 3, <= 192 rows 32 ring 3,
   //     then rows 48 ring 3 where those number <= 256 (one per CU), else
-  //     rows 48 ring 2 (M 16 N 6144 split_k 2 / 4 / 8: 11.6 / 12.3 / 15.5
-  //     us; split_k 2 with rows 16 ring 2 12.6, M 8 11.4 against 11.6; in
-  //     two or more rounds rows 48 ring 2 beat rows 32 ring 2 by 1.6-3 %:
-  //     M 16 N 12288 / 24576 split_k 2 19.3 / 36.7 against 19.9 / 37.7);
+  //     rows 48 ring 2 up to split_k 4 and rows 32 ring 2 above (M 16 N 6144
+  //     split_k 2 / 4 / 8: 11.6 / 12.3 / 15.5 us; split_k 2 with rows 16
+  //     ring 2 12.6, M 8 11.4 against 11.6; in two or more rounds rows 48
+  //     ring 2 beat rows 32 ring 2 by 1.6-3 % at split_k 2 and 4, M 16
+  //     N 12288 / 24576 split_k 2 19.3 / 36.7 against 19.9 / 37.7, and lose
+  //     by 5 % at split_k 8, M 8 / 16 N 6144 15.6 / 16.4 against 14.9 / 15.6);
   //   - split_k 1, M > 32 (where the quarter-rows tiles above do not
   //     apply): the tile width of 16..64 rows with the fewest rounds of 256
   //     workgroups times rows loaded per K step (activation blocks plus
@@ -220,7 +222,8 @@ int pick(int M, int N, int K, int S, lowm_tactic* t, bool push = false) {
     } else if (M > 4 && M <= 16) {
       if (w32 <= 96 ? quarter(16, 3)
                     : w32 <= 192 ? quarter(32, 3)
-                                 : w48 <= 256 ? quarter(48, 3) : quarter(48, 2))
+                                 : w48 <= 256 ? quarter(48, 3)
+                                              : S <= 4 ? quarter(48, 2) : quarter(32, 2))
         return LOWM_OK;
     } else if (M > 16 && M <= 32 && S == 1) {
       if (w16 <= 192 ? quarter(16, 3) : (quarter(32, 4) || quarter(32, 3))) return LOWM_OK;

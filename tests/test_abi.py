@@ -144,7 +144,7 @@ def test_pick_quarter_tiles_where_measured_faster(lib):
             (16, 6144, 4096, 4, 48, 2),      # 768 32-row, 512 48-row workgroups
             (16, 1536, 8192, 2, 16, 3),      # 96
             (8, 1536, 8192, 4, 32, 3),       # 192
-            (12, 6144, 4096, 8, 48, 2),      # 1536 32-row workgroups
+            (12, 6144, 4096, 8, 32, 2),      # split_k 8: 32-row tiles, ring 2
             (32, 6144, 4096, 1, 32, 4),      # 384 16-row workgroups
             (24, 6144, 4096, 2, 48, 3),      # 256 48-row workgroups
             (24, 12288, 4096, 2, 48, 3),     # fewest rounds x rows: 48 rows, two rounds
