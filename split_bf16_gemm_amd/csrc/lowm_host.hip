@@ -283,15 +283,15 @@ constexpr unsigned char kBestSplit[kSplitRows][6][4] = {
      {1, 1, 2, 8}},   // N 24576
     // 4 < M <= 8
     {{4, 4, 8, 8},
-     {2, 4, 4, 4},
-     {2, 4, 4, 4},
+     {2, 8, 4, 4},
+     {2, 2, 4, 4},
      {1, 1, 2, 4},
-     {1, 2, 2, 4},
+     {1, 1, 2, 4},
      {1, 1, 2, 4}},
     // 8 < M <= 16
     {{4, 4, 8, 8},
-     {2, 4, 4, 8},
-     {1, 4, 4, 4},
+     {4, 4, 4, 8},
+     {2, 4, 4, 4},
      {1, 1, 2, 4},
      {1, 2, 2, 4},
      {1, 1, 2, 4}},
